@@ -1,0 +1,277 @@
+"""Benchmark of the blockwise-scaled FP8 training hot path on one MI355X.
+
+One step = every kernel of one blockwise-FP8 linear layer's training pass
+over one batch of seeded synthetic data already resident in HBM:
+
+  quantize A [M, K] rows + transposed columns (1x128),
+  quantize W [N, K] (128x128) and W^T (3-D colwise, G = 1),
+  quantize grad_out [M, N] rows + transposed columns (1x128),
+  forward  out     = A . W^T          (1x128 x 128x128),
+  dgrad    grad_in = grad_out . W     (1x128 x 128x128, via W^T),
+  wgrad    grad_W  = grad_out^T . A   (1x128 x 1x128).
+
+For the MoE workload the GEMMs are the grouped forms (GROUP_M forward and
+dgrad, GROUP_K wgrad) and W is quantized per expert.
+
+Prints ONE JSON line.  `value` is fwd+bwd GEMM FLOPs (3 * 2*M*N*K) divided
+by the wall time of the whole step (quantizers included).  Per-kernel times
+come from HIP events recorded on the launch stream around every kernel of
+every timed step.  The CPU oracle is timed on a bounded sample of the same
+workload on the host (rank 0, N = 1).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import blockwise_scaled_fp8_bs_amd as bs  # noqa: E402
+from blockwise_scaled_fp8_bs_amd import inputs  # noqa: E402
+
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA (no sparsity)
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+DEFAULT_WORKLOAD = "dense_8192x4096x4096"
+
+
+def r4(n):
+    return (n + 3) // 4 * 4
+
+
+class Step:
+    """Buffers and launches of one training step of one workload."""
+
+    def __init__(self, w: inputs.Workload, seed=0, device="cuda"):
+        self.w = w
+        M, K, N, G = w.M, w.K, w.N, w.G
+        dev = device
+        a, wt, gout, ends = inputs.make_operands(w, seed=seed, device=dev)
+        self.a, self.wt, self.gout = a, wt, gout
+        self.grouped = G > 1
+        u8 = torch.uint8
+        # activations: rows (forward A operand) and transposed columns (wgrad B operand)
+        self.qa = torch.empty((M, K), dtype=u8, device=dev)
+        self.sa = torch.empty((K // 128, r4(M)), dtype=torch.float32, device=dev)
+        self.qaT = torch.empty((K, M), dtype=u8, device=dev)
+        self.saT = torch.empty((M // 128, r4(K)), dtype=torch.float32, device=dev)
+        # grad_out: rows (dgrad A operand) and transposed columns (wgrad A operand)
+        self.qg = torch.empty((M, N), dtype=u8, device=dev)
+        self.sg = torch.empty((N // 128, r4(M)), dtype=torch.float32, device=dev)
+        self.qgT = torch.empty((N, M), dtype=u8, device=dev)
+        self.sgT = torch.empty((M // 128, r4(N)), dtype=torch.float32, device=dev)
+        # weights: [G*N, K] 128x128 (forward) and [G, K, N] transposed (dgrad)
+        wv = wt.view(G * N, K)
+        self.wv = wv
+        self.qw = torch.empty((G * N, K), dtype=u8, device=dev)
+        self.sw = torch.empty((K // 128, r4(G * N // 128)), dtype=torch.float32, device=dev)
+        self.qwT = torch.empty((G, K, N), dtype=u8, device=dev)
+        self.swT = torch.empty((G, N // 128, r4(K // 128)), dtype=torch.float32, device=dev)
+        self.w3 = wt.view(G, N, K)
+        # outputs
+        self.out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        self.gin = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        self.gw = torch.empty((G, N, K) if self.grouped else (N, K), dtype=torch.bfloat16, device=dev)
+        if self.grouped:
+            self.ends = torch.tensor(ends, dtype=torch.int32, device=dev)
+            self.group_sizes = [e - s for s, e in zip([0] + ends[:-1], ends)]
+            self.sw_view = torch.as_strided(self.sw, (G, K // 128, N // 128), (N // 128, self.sw.stride(0), 1))
+
+    # (name, fn, algorithmic bytes or flops, kind)
+    def kernels(self):
+        w = self.w
+        M, K, N, G = w.M, w.K, w.N, w.G
+        gemm_flops = 2.0 * M * N * K
+        q1_bytes = lambda R, C: R * C * (2 + 2) + 4 * (R * C // 128) * 2  # noqa: E731
+        q128_bytes = lambda R, C: R * C * 3 + 4 * (R * C // 16384)  # noqa: E731
+        ks = [
+            ("quant_1x128_rowcol(A)", lambda: bs.bs_quant_1x128(self.a, self.qa, self.sa, self.qaT, self.saT),
+             q1_bytes(M, K), "GB/s"),
+            ("quant_128x128(W)", lambda: bs.bs_quant_128x128(self.wv, self.qw, self.sw), q128_bytes(G * N, K), "GB/s"),
+            ("quant_3d_colwise(W)", lambda: bs.bs_quant_3d_colwise(self.w3, self.qwT, self.swT),
+             q128_bytes(G * N, K), "GB/s"),
+            ("quant_1x128_rowcol(grad_out)",
+             lambda: bs.bs_quant_1x128(self.gout, self.qg, self.sg, self.qgT, self.sgT), q1_bytes(M, N), "GB/s"),
+        ]
+        if not self.grouped:
+            ks += [
+                ("gemm_fwd", lambda: bs.bs_scaled_mm(self.qa, self.sa, self.qw, self.sw, bs.BS_SCALE_128X128,
+                                                     out=self.out), gemm_flops, "TFLOP/s"),
+                ("gemm_dgrad", lambda: bs.bs_scaled_mm(self.qg, self.sg, self.qwT[0], self.swT[0],
+                                                       bs.BS_SCALE_128X128, out=self.gin), gemm_flops, "TFLOP/s"),
+                ("gemm_wgrad", lambda: bs.bs_scaled_mm(self.qgT, self.sgT, self.qaT, self.saT, bs.BS_SCALE_1X128,
+                                                       out=self.gw), gemm_flops, "TFLOP/s"),
+            ]
+        else:
+            ks += [
+                ("grouped_gemm_fwd", lambda: bs.bs_grouped_scaled_mm(
+                    bs.BS_GROUP_M, self.ends, self.qa, self.sa, self.qw.view(G, N, K), self.sw_view,
+                    bs.BS_SCALE_128X128, out=self.out), gemm_flops, "TFLOP/s"),
+                ("grouped_gemm_dgrad", lambda: bs.bs_grouped_scaled_mm(
+                    bs.BS_GROUP_M, self.ends, self.qg, self.sg, self.qwT, self.swT, bs.BS_SCALE_128X128,
+                    out=self.gin), gemm_flops, "TFLOP/s"),
+                ("grouped_gemm_wgrad", lambda: bs.bs_grouped_scaled_mm(
+                    bs.BS_GROUP_K, self.ends, self.qgT, self.sgT, self.qaT, self.saT, bs.BS_SCALE_1X128,
+                    out=self.gw), gemm_flops, "TFLOP/s"),
+            ]
+        return ks
+
+
+def cpu_oracle_sample(w: inputs.Workload, rows=512, seed=0):
+    """Time the CPU oracle on a bounded sample of the workload.
+
+    The sample is the first `rows` tokens of the same seeded inputs (a
+    [rows, K] activation and [rows, N] grad_out; the full weight, or one
+    expert's weight): all seven steps (four quantizers, three GEMMs over the
+    sampled tokens).  Returns (TFLOP/s of the sampled GEMMs over the whole
+    sample time, seconds, description).
+    """
+    import numpy as np
+    from oracle import gemm, quant
+
+    a, wt, gout, _ = inputs.make_operands(w, seed=seed, device="cpu", rows=rows)
+    if w.G > 1:
+        wt = wt[0]
+    bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+    t0 = time.perf_counter()
+    qa, sa = quant.quant_1x128_rowwise(bits(a))
+    qaT, saT = quant.quant_1x128_colwise(bits(a))
+    qw, sw = quant.quant_128x128(bits(wt))
+    qwT, swT = quant.quant_3d_colwise(bits(wt)[None])
+    qg, sg = quant.quant_1x128_rowwise(bits(gout))
+    qgT, sgT = quant.quant_1x128_colwise(bits(gout))
+    gemm.scaled_mm(qa, sa, qw, sw, 128)
+    gemm.scaled_mm(qg, sg, qwT[0], swT[0], 128)
+    gemm.scaled_mm(qgT, sgT, qaT, saT, 1)
+    dt = time.perf_counter() - t0
+    flops = 3 * 2.0 * rows * w.N * w.K
+    desc = (f"first {rows} of {w.M} tokens of {w.name}{' (expert 0 weight)' if w.G > 1 else ''}: "
+            f"4 quantizers + fwd/dgrad/wgrad GEMMs, {flops / 1e9:.1f} GFLOP")
+    return flops / dt / 1e12, dt, desc
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return os.cpu_count()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(inputs.WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=512)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the blockwise FP8 hot path here is a single-GPU build "
+              "(no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    w = inputs.WORKLOADS[args.workload]
+    if w.fwd_only:
+        print("the forward-only workload is a parity case, not a bench line", file=sys.stderr)
+        sys.exit(2)
+    torch.manual_seed(args.seed)
+    step = Step(w, seed=args.seed)
+    ks = step.kernels()
+    stream = torch.cuda.current_stream()
+
+    def run_step(events=None):
+        for i, (_, fn, _, _) in enumerate(ks):
+            if events is not None:
+                events[i][0].record(stream)
+            fn()
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in ks]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        run_step(ev[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    per_kernel = {}
+    for i, (name, _, work, unit) in enumerate(ks):
+        ms = sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)) / args.steps
+        rate = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+        peak = FP8_PEAK_TFLOPS if unit == "TFLOP/s" else HBM_PEAK_GBS
+        per_kernel[name] = {"ms": round(ms, 4), "rate": round(rate, 1), "unit": unit,
+                            "frac": round(rate / peak, 4), "work": work}
+    gemm_flops = 3 * 2.0 * w.M * w.N * w.K
+    value = gemm_flops / (ms_per_step * 1e-3) / 1e12
+    gemm_ms = sum(v["ms"] for v in per_kernel.values() if v["unit"] == "TFLOP/s")
+    quant_ms = sum(v["ms"] for v in per_kernel.values() if v["unit"] == "GB/s")
+    quant_bytes = sum(v["work"] for v in per_kernel.values() if v["unit"] == "GB/s")
+    dom = max(per_kernel, key=lambda k: per_kernel[k]["ms"])
+    d = per_kernel[dom]
+    roofline = {
+        "kernel": dom,
+        "bound": "mfma" if d["unit"] == "TFLOP/s" else "hbm",
+        "achieved": d["rate"],
+        "peak": FP8_PEAK_TFLOPS if d["unit"] == "TFLOP/s" else HBM_PEAK_GBS,
+        "unit": d["unit"],
+        "frac": d["frac"],
+        "traffic": None,
+    }
+    for v in per_kernel.values():
+        v.pop("work")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        tflops, secs, desc = cpu_oracle_sample(w, rows=args.cpu_rows, seed=args.seed)
+        cpu = {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+               "sample": desc, "seconds": round(secs, 2)}
+
+    line = {
+        "metric": "FP8 blockwise GEMM TFLOP/s fwd+bwd, % of FP8 MFMA peak; quantizer GB/s",
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic (seeded N(0, s) bf16, resident in HBM)",
+        "config": {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "G": w.G,
+                   "step": "quant A/W/W^T/grad_out + fwd, dgrad, wgrad GEMMs"},
+        "gemm_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1),
+        "gemm_frac_of_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+        "quant_gbs": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
+        "quant_frac_of_hbm": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernels": per_kernel,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,24 @@
+"""Blockwise-scaled FP8 linear-layer training kernels for AMD MI355X (gfx950).
+
+The compute path is the HIP library ``libbs.so`` (C ABI in include/bs.h);
+``binding`` marshals torch tensors into it.  Importing this package does not
+load the library; the first call does, and raises if it has not been built.
+"""
+
+from .binding import (  # noqa: F401
+    BS_GROUP_K,
+    BS_GROUP_M,
+    BS_OUT_BF16,
+    BS_OUT_F32,
+    BS_SCALE_128X128,
+    BS_SCALE_1X128,
+    BsError,
+    bs_diag_division,
+    bs_diag_e4m3_census,
+    bs_grouped_scaled_mm,
+    bs_quant_128x128,
+    bs_quant_1x128,
+    bs_quant_3d_colwise,
+    bs_scaled_mm,
+    empty_scales,
+)

@@ -1,0 +1,262 @@
+"""Thin Python binding of the C ABI (include/bs.h), same names, torch tensors in.
+
+Argument marshalling only: shapes, strides and data pointers of torch tensors
+are passed to the HIP library, whose kernels do all of the work; torch
+provides device memory and the current stream.  Layout rules are checked here
+and again in the library; a tensor in the wrong layout raises ``ValueError``
+instead of being copied ("add FSDP and TP tests for Float8BlockwiseLinear",
+review thread on the layout assertions: fail loudly, never silently copy).
+
+Tensor conventions (all on one GPU):
+
+* bf16 input ``x``: torch.bfloat16, 2-D (or 3-D for expert weights), unit
+  stride along the last dimension; its row stride is the ``ld``.
+* e4m3 codes: torch.uint8 with the same convention.
+* scales: torch.float32, 2-D ``[K/128, ld]`` (3-D ``[G, K/128, ld]`` per
+  expert): the contraction-block index is the outer index ("K-major"), the
+  row stride is ``ld_s`` (a multiple of 4); entries past the logical count
+  are padding and are never written.
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+BS_SCALE_1X128 = 4
+BS_SCALE_128X128 = 5
+BS_OUT_BF16 = 0
+BS_OUT_F32 = 1
+BS_GROUP_M = 0
+BS_GROUP_K = 1
+
+
+class BsError(RuntimeError):
+    """A nonzero bs_status from the library."""
+
+    def __init__(self, status, fn):
+        lib = _lib.load()
+        self.status = status
+        self.name = lib.bs_status_string(status).decode()
+        super().__init__(f"{fn} failed with {self.name}: {lib.bs_last_error().decode()}")
+
+
+def _check(status, fn):
+    if status != 0:
+        raise BsError(status, fn)
+
+
+def _ptr(t):
+    # tensors without elements may have no storage: pass NULL (the ABI allows
+    # NULL exactly for tensors with no elements)
+    return None if t is None or t.data_ptr() == 0 else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _require(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _mat(t, name, dtype, dims=2):
+    _require(t is not None, f"{name} is required")
+    _require(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    _require(t.dim() == dims, f"{name} must be {dims}-D, got shape {tuple(t.shape)}")
+    _require(t.is_cuda, f"{name} must be a GPU tensor")
+    _require(t.shape[-1] <= 1 or t.stride(-1) == 1,
+             f"{name} must have unit stride along its last dimension (row-major); got strides {t.stride()}"
+             " -- pass a tensor in the required layout instead of relying on a copy")
+    return t
+
+
+def _ld(t):
+    return t.stride(-2)
+
+
+def _scale(t, name, nkb, count):
+    _mat(t, name, torch.float32)
+    _require(t.shape[0] == nkb, f"{name} must have {nkb} rows (one per 128-block of the contraction), got {t.shape[0]}")
+    _require(t.shape[1] >= count, f"{name} must have at least {count} columns (K-major [K/128][>= {count}])")
+    return t.stride(0)
+
+
+def _round4(n):
+    return (n + 3) // 4 * 4
+
+
+def empty_scales(nkb, count, device, pad=0):
+    """Allocate a K-major scale tensor [nkb, roundup4(count) + pad] (float32)."""
+    return torch.empty((nkb, _round4(count) + pad), dtype=torch.float32, device=device)
+
+
+# ----------------------------------------------------------------------------
+# quantizers
+# ----------------------------------------------------------------------------
+
+def bs_quant_1x128(x, q_row=None, s_row=None, q_col=None, s_col=None, stream=None):
+    """1x128 quantizer (rows and/or transposed columns) in one pass.
+
+    x [R, C] bf16; q_row [R, C] uint8 with s_row [C/128, >= R];
+    q_col [C, R] uint8 with s_col [R/128, >= C].
+    """
+    _mat(x, "x", torch.bfloat16)
+    R, C = x.shape
+    args = [_ptr(x), R, C, _ld(x)]
+    if q_row is not None or s_row is not None:
+        _mat(q_row, "q_row", torch.uint8)
+        _require(tuple(q_row.shape) == (R, C), f"q_row must be [{R}, {C}]")
+        ld_sr = _scale(s_row, "s_row", C // 128, R)
+        args += [_ptr(q_row), _ld(q_row), _ptr(s_row), ld_sr]
+    else:
+        args += [None, 0, None, 0]
+    if q_col is not None or s_col is not None:
+        _mat(q_col, "q_col", torch.uint8)
+        _require(tuple(q_col.shape) == (C, R), f"q_col must be the transpose [{C}, {R}]")
+        ld_sc = _scale(s_col, "s_col", R // 128, C)
+        args += [_ptr(q_col), _ld(q_col), _ptr(s_col), ld_sc]
+    else:
+        args += [None, 0, None, 0]
+    _check(_lib.load().bs_quant_1x128(*args, _stream(stream)), "bs_quant_1x128")
+
+
+def bs_quant_128x128(x, q, s, stream=None):
+    """128x128 quantizer: x [R, C] bf16 -> q [R, C] uint8, s [C/128, >= R/128]."""
+    _mat(x, "x", torch.bfloat16)
+    _mat(q, "q", torch.uint8)
+    R, C = x.shape
+    _require(tuple(q.shape) == (R, C), f"q must be [{R}, {C}]")
+    ld_s = _scale(s, "s", C // 128, R // 128)
+    _check(_lib.load().bs_quant_128x128(_ptr(x), R, C, _ld(x), _ptr(q), _ld(q), _ptr(s), ld_s, _stream(stream)),
+           "bs_quant_128x128")
+
+
+def bs_quant_3d_colwise(x, q, s, stream=None):
+    """3-D colwise quantizer: x [G, R, C] bf16 -> q [G, C, R] uint8,
+    s [G, R/128, >= C/128] (K-major for the transposed operand)."""
+    _mat(x, "x", torch.bfloat16, 3)
+    _mat(q, "q", torch.uint8, 3)
+    _mat(s, "s", torch.float32, 3)
+    G, R, C = x.shape
+    _require(tuple(q.shape) == (G, C, R), f"q must be [{G}, {C}, {R}]")
+    _require(s.shape[0] == G and s.shape[1] == R // 128 and s.shape[2] >= C // 128,
+             f"s must be [{G}, {R // 128}, >= {C // 128}]")
+    ld_s = s.stride(1)
+    _check(_lib.load().bs_quant_3d_colwise(_ptr(x), G, R, C, x.stride(0), _ld(x), _ptr(q), q.stride(0), _ld(q),
+                                           _ptr(s), s.stride(0), ld_s, _stream(stream)),
+           "bs_quant_3d_colwise")
+
+
+# ----------------------------------------------------------------------------
+# GEMMs
+# ----------------------------------------------------------------------------
+
+def bs_scaled_mm(a, sa, b, sb, b_kind, out=None, out_dtype=torch.bfloat16, stream=None):
+    """D[M, N] = blockwise-scaled A [M, K] . B [N, K]^T.
+
+    sa [K/128, >= M] (1x128); sb [K/128, >= N/128] for BS_SCALE_128X128 or
+    [K/128, >= N] for BS_SCALE_1X128.  Returns ``out`` ([M, N], bf16 or fp32).
+    """
+    _mat(a, "a", torch.uint8)
+    _mat(b, "b", torch.uint8)
+    M, K = a.shape
+    N, Kb = b.shape
+    _require(K == Kb, f"a is [M, {K}] but b is [N, {Kb}]: both must be contiguous along the same K")
+    ld_sa = _scale(sa, "sa", K // 128, M)
+    ld_sb = _scale(sb, "sb", K // 128, N if b_kind == BS_SCALE_1X128 else (N + 127) // 128)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _mat(out, "out", out.dtype)
+    _require(tuple(out.shape) == (M, N), f"out must be [{M}, {N}]")
+    dt = {torch.bfloat16: BS_OUT_BF16, torch.float32: BS_OUT_F32}.get(out.dtype)
+    _require(dt is not None, "out must be bfloat16 or float32")
+    _check(_lib.load().bs_scaled_mm(M, N, K, _ptr(a), _ld(a), _ptr(sa), ld_sa, BS_SCALE_1X128, _ptr(b), _ld(b),
+                                    _ptr(sb), ld_sb, b_kind, _ptr(out), _ld(out), dt, _stream(stream)),
+           "bs_scaled_mm")
+    return out
+
+
+def bs_grouped_scaled_mm(mode, group_end, a, sa, b, sb, b_kind, out=None, out_dtype=torch.bfloat16,
+                         stream=None):
+    """Grouped (MoE) scaled GEMM.
+
+    BS_GROUP_M: a [M, K], sa [K/128, >= M]; b [G, N, K] (any stride between
+      experts); sb [G, K/128, >= N/128] (any stride between experts, e.g. an
+      interleaved view of one [K/128, G*N/128] scale matrix); out [M, N].
+    BS_GROUP_K: a [M, T], sa [T/128, >= M]; b [N, T], sb [T/128, >= N];
+      out [G, M, N]; group g contracts over tokens [end_{g-1}, end_g).
+    group_end: int32 GPU tensor [G] of cumulative ends.
+    """
+    _require(group_end is not None and group_end.dtype == torch.int32 and group_end.is_cuda
+             and group_end.dim() == 1, "group_end must be a 1-D int32 GPU tensor")
+    G = group_end.shape[0]
+    _require(group_end.stride(0) == 1 or G <= 1, "group_end must be contiguous")
+    _mat(a, "a", torch.uint8)
+    M, K = a.shape
+    dt_map = {torch.bfloat16: BS_OUT_BF16, torch.float32: BS_OUT_F32}
+    if mode == BS_GROUP_M:
+        _mat(b, "b", torch.uint8, 3)
+        _require(b.shape[0] == G and b.shape[2] == K, f"b must be [{G}, N, {K}]")
+        N = b.shape[1]
+        _mat(sb, "sb", torch.float32, 3)
+        _require(sb.shape[0] == G and sb.shape[1] == K // 128 and sb.shape[2] >= N // 128,
+                 f"sb must be [{G}, {K // 128}, >= {N // 128}]")
+        ld_sa = _scale(sa, "sa", K // 128, M)
+        if out is None:
+            out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+        _mat(out, "out", out.dtype)
+        _require(tuple(out.shape) == (M, N), f"out must be [{M}, {N}]")
+        dt = dt_map.get(out.dtype)
+        _require(dt is not None, "out must be bfloat16 or float32")
+        ld_sb = sb.stride(1)
+        args = [mode, G, M, N, K, _ptr(group_end), _ptr(a), _ld(a), _ptr(sa), ld_sa,
+                _ptr(b), b.stride(0), b.stride(1), _ptr(sb), sb.stride(0), ld_sb, b_kind,
+                _ptr(out), 0, _ld(out), dt]
+    else:
+        _mat(b, "b", torch.uint8)
+        N, Kb = b.shape
+        _require(Kb == K, f"b must be [N, {K}] (tokens contiguous)")
+        ld_sa = _scale(sa, "sa", K // 128, M)
+        ld_sb = _scale(sb, "sb", K // 128, N)
+        if out is None:
+            out = torch.empty((G, M, N), dtype=out_dtype, device=a.device)
+        _mat(out, "out", out.dtype, 3)
+        _require(tuple(out.shape) == (G, M, N), f"out must be [{G}, {M}, {N}]")
+        dt = dt_map.get(out.dtype)
+        _require(dt is not None, "out must be bfloat16 or float32")
+        args = [mode, G, M, N, K, _ptr(group_end), _ptr(a), _ld(a), _ptr(sa), ld_sa,
+                _ptr(b), 0, _ld(b), _ptr(sb), 0, ld_sb, b_kind,
+                _ptr(out), out.stride(0), out.stride(1), dt]
+    _check(_lib.load().bs_grouped_scaled_mm(*args, _stream(stream)), "bs_grouped_scaled_mm")
+    return out
+
+
+# ----------------------------------------------------------------------------
+# diagnostics
+# ----------------------------------------------------------------------------
+
+def bs_diag_e4m3_census(device="cuda", stream=None):
+    """(min_bits, max_bits, counts) per e4m3 code over all |y| <= 448 (CPU tensors)."""
+    mn = torch.empty(256, dtype=torch.int32, device=device)
+    mx = torch.empty(256, dtype=torch.int32, device=device)
+    cnt = torch.empty(256, dtype=torch.int64, device=device)
+    _check(_lib.load().bs_diag_e4m3_census(_ptr(mn), _ptr(mx), _ptr(cnt), _stream(stream)), "bs_diag_e4m3_census")
+    torch.cuda.synchronize()
+    return mn.cpu(), mx.cpu(), cnt.cpu()
+
+
+def bs_diag_division(device="cuda", stream=None):
+    """Counts of the quantizers' division vs IEEE (see include/bs.h):
+    dict with pairs, scale_mismatch, code_mismatch, quotient_mismatch,
+    tiny_quotient_mismatch."""
+    res = torch.zeros(5, dtype=torch.int64, device=device)
+    _check(_lib.load().bs_diag_division(_ptr(res), _stream(stream)), "bs_diag_division")
+    torch.cuda.synchronize()
+    v = [int(t) for t in res.cpu().tolist()]
+    return dict(zip(["pairs", "scale_mismatch", "code_mismatch", "quotient_mismatch",
+                     "tiny_quotient_mismatch"], v))

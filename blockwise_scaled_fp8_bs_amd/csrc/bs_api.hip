@@ -1,0 +1,290 @@
+// C ABI of the blockwise-scaled FP8 library: host-side validation, then one
+// launch on the caller's stream.  Declarations and contracts: include/bs.h.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/bs.h"
+#include "bs_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bs_status fail(bs_status st, const char* fn, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = std::string(fn) + ": " + buf;
+    return st;
+}
+
+bs_status ok() {
+    g_last_error.clear();
+    return BS_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bs_status hip_status(hipError_t e, const char* fn) {
+    if (e == hipSuccess) return ok();
+    return fail(BS_ERR_HIP, fn, "kernel launch failed: %s", hipGetErrorString(e));
+}
+
+// Leading dimension checks, in elements.
+#define REQUIRE(cond, code, ...)                           \
+    do {                                                   \
+        if (!(cond)) return fail(code, fn, __VA_ARGS__);   \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* bs_status_string(bs_status st) {
+    switch (st) {
+        case BS_OK: return "BS_OK";
+        case BS_ERR_NULL: return "BS_ERR_NULL";
+        case BS_ERR_SHAPE: return "BS_ERR_SHAPE";
+        case BS_ERR_LAYOUT: return "BS_ERR_LAYOUT";
+        case BS_ERR_ALIGN: return "BS_ERR_ALIGN";
+        case BS_ERR_MODE: return "BS_ERR_MODE";
+        case BS_ERR_HIP: return "BS_ERR_HIP";
+    }
+    return "BS_ERR_UNKNOWN";
+}
+
+const char* bs_last_error(void) { return g_last_error.c_str(); }
+
+bs_status bs_quant_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x, uint8_t* q_row, int64_t ld_qr,
+                         float* s_row, int64_t ld_sr, uint8_t* q_col, int64_t ld_qc, float* s_col, int64_t ld_sc,
+                         hipStream_t stream) {
+    static const char* fn = "bs_quant_1x128";
+    const bool row = q_row || s_row, col = q_col || s_col;
+    const bool empty = R == 0 || C == 0;
+    REQUIRE(x || empty, BS_ERR_NULL, "x is NULL");
+    REQUIRE(!row || (q_row && s_row) || empty, BS_ERR_NULL, "q_row and s_row must both be set or both NULL");
+    REQUIRE(!col || (q_col && s_col) || empty, BS_ERR_NULL, "q_col and s_col must both be set or both NULL");
+    REQUIRE(row || col || empty, BS_ERR_NULL, "no output requested (q_row/s_row and q_col/s_col are all NULL)");
+    REQUIRE(R >= 0 && C >= 0, BS_ERR_SHAPE, "R=%lld C=%lld must be >= 0", (long long)R, (long long)C);
+    REQUIRE(C % 128 == 0, BS_ERR_SHAPE, "C=%lld must be a multiple of 128 (1x128 blocks along rows)",
+            (long long)C);
+    REQUIRE(!col || R % 128 == 0, BS_ERR_SHAPE,
+            "R=%lld must be a multiple of 128 for the column output (128-row blocks)", (long long)R);
+    REQUIRE(ld_x >= C, BS_ERR_LAYOUT, "ld_x=%lld < C=%lld: x must be row-major [R, C]", (long long)ld_x,
+            (long long)C);
+    REQUIRE(aligned16(x) && ld_x % 8 == 0, BS_ERR_ALIGN, "x must be 16-byte aligned with ld_x %% 8 == 0");
+    if (row) {
+        REQUIRE(ld_qr >= C, BS_ERR_LAYOUT, "ld_qr=%lld < C=%lld: q_row is row-major [R, C]", (long long)ld_qr,
+                (long long)C);
+        REQUIRE(ld_sr >= R, BS_ERR_LAYOUT, "ld_sr=%lld < R=%lld: s_row is K-major [C/128][ld_sr >= R]",
+                (long long)ld_sr, (long long)R);
+        REQUIRE(ld_sr % 4 == 0, BS_ERR_LAYOUT, "ld_sr=%lld must be a multiple of 4 (16-byte scale rows)",
+                (long long)ld_sr);
+        REQUIRE(aligned16(q_row) && ld_qr % 16 == 0, BS_ERR_ALIGN,
+                "q_row must be 16-byte aligned with ld_qr %% 16 == 0");
+        REQUIRE(aligned16(s_row), BS_ERR_ALIGN, "s_row must be 16-byte aligned");
+    }
+    if (col) {
+        REQUIRE(ld_qc >= R, BS_ERR_LAYOUT, "ld_qc=%lld < R=%lld: q_col is the transpose [C, R]",
+                (long long)ld_qc, (long long)R);
+        REQUIRE(ld_sc >= C, BS_ERR_LAYOUT, "ld_sc=%lld < C=%lld: s_col is K-major [R/128][ld_sc >= C]",
+                (long long)ld_sc, (long long)C);
+        REQUIRE(ld_sc % 4 == 0, BS_ERR_LAYOUT, "ld_sc=%lld must be a multiple of 4 (16-byte scale rows)",
+                (long long)ld_sc);
+        REQUIRE(aligned16(q_col) && ld_qc % 16 == 0, BS_ERR_ALIGN,
+                "q_col must be 16-byte aligned with ld_qc %% 16 == 0");
+        REQUIRE(aligned16(s_col), BS_ERR_ALIGN, "s_col must be 16-byte aligned");
+    }
+    if (R == 0 || C == 0) return ok();
+    bs::Quant1x128Args a{x, R, C, ld_x, q_row, ld_qr, s_row, ld_sr, q_col, ld_qc, s_col, ld_sc, C / 128};
+    return hip_status(bs::launch_quant_1x128(a, row, col, stream), fn);
+}
+
+bs_status bs_quant_128x128(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x, uint8_t* q, int64_t ld_q,
+                           float* s, int64_t ld_s, hipStream_t stream) {
+    static const char* fn = "bs_quant_128x128";
+    REQUIRE((x && q && s) || R == 0 || C == 0, BS_ERR_NULL, "x, q and s must be non-NULL");
+    REQUIRE(R >= 0 && C >= 0 && R % 128 == 0 && C % 128 == 0, BS_ERR_SHAPE,
+            "R=%lld C=%lld must be non-negative multiples of 128 (128x128 blocks)", (long long)R, (long long)C);
+    REQUIRE(ld_x >= C, BS_ERR_LAYOUT, "ld_x=%lld < C=%lld: x must be row-major [R, C]", (long long)ld_x,
+            (long long)C);
+    REQUIRE(ld_q >= C, BS_ERR_LAYOUT, "ld_q=%lld < C=%lld: q is row-major [R, C]", (long long)ld_q, (long long)C);
+    REQUIRE(ld_s >= R / 128, BS_ERR_LAYOUT, "ld_s=%lld < R/128=%lld: s is K-major [C/128][ld_s >= R/128]",
+            (long long)ld_s, (long long)(R / 128));
+    REQUIRE(ld_s % 4 == 0, BS_ERR_LAYOUT, "ld_s=%lld must be a multiple of 4 (K stride padded to 16 bytes)",
+            (long long)ld_s);
+    REQUIRE(aligned16(x) && ld_x % 8 == 0, BS_ERR_ALIGN, "x must be 16-byte aligned with ld_x %% 8 == 0");
+    REQUIRE(aligned16(q) && ld_q % 16 == 0, BS_ERR_ALIGN, "q must be 16-byte aligned with ld_q %% 16 == 0");
+    REQUIRE(aligned16(s), BS_ERR_ALIGN, "s must be 16-byte aligned");
+    if (R == 0 || C == 0) return ok();
+    bs::Quant128Args a{x, 1, R, C, 0, ld_x, q, 0, ld_q, s, 0, ld_s, R / 128, C / 128};
+    return hip_status(bs::launch_quant_128x128(a, false, stream), fn);
+}
+
+bs_status bs_quant_3d_colwise(const uint16_t* x, int64_t G, int64_t R, int64_t C, int64_t stride_xg, int64_t ld_x,
+                              uint8_t* q, int64_t stride_qg, int64_t ld_q, float* s, int64_t stride_sg, int64_t ld_s,
+                              hipStream_t stream) {
+    static const char* fn = "bs_quant_3d_colwise";
+    REQUIRE((x && q && s) || G == 0 || R == 0 || C == 0, BS_ERR_NULL, "x, q and s must be non-NULL");
+    REQUIRE(G >= 0 && R >= 0 && C >= 0 && R % 128 == 0 && C % 128 == 0, BS_ERR_SHAPE,
+            "G=%lld R=%lld C=%lld: G >= 0 and R, C non-negative multiples of 128", (long long)G, (long long)R,
+            (long long)C);
+    REQUIRE(ld_x >= C, BS_ERR_LAYOUT, "ld_x=%lld < C=%lld: x[g] must be row-major [R, C]", (long long)ld_x,
+            (long long)C);
+    REQUIRE(G <= 1 || stride_xg >= R * ld_x, BS_ERR_LAYOUT, "stride_xg=%lld < R*ld_x", (long long)stride_xg);
+    REQUIRE(ld_q >= R, BS_ERR_LAYOUT, "ld_q=%lld < R=%lld: q[g] is the transpose [C, R]", (long long)ld_q,
+            (long long)R);
+    REQUIRE(G <= 1 || stride_qg >= C * ld_q, BS_ERR_LAYOUT, "stride_qg=%lld < C*ld_q", (long long)stride_qg);
+    REQUIRE(ld_s >= C / 128, BS_ERR_LAYOUT, "ld_s=%lld < C/128=%lld: s[g] is K-major [R/128][ld_s >= C/128]",
+            (long long)ld_s, (long long)(C / 128));
+    REQUIRE(ld_s % 4 == 0, BS_ERR_LAYOUT, "ld_s=%lld must be a multiple of 4", (long long)ld_s);
+    REQUIRE(G <= 1 || stride_sg >= (R / 128) * ld_s, BS_ERR_LAYOUT, "stride_sg=%lld < (R/128)*ld_s",
+            (long long)stride_sg);
+    REQUIRE(stride_sg % 4 == 0 && stride_qg % 16 == 0 && stride_xg % 8 == 0, BS_ERR_ALIGN,
+            "group strides must keep 16-byte alignment (stride_sg %% 4, stride_qg %% 16, stride_xg %% 8)");
+    REQUIRE(aligned16(x) && ld_x % 8 == 0, BS_ERR_ALIGN, "x must be 16-byte aligned with ld_x %% 8 == 0");
+    REQUIRE(aligned16(q) && ld_q % 16 == 0, BS_ERR_ALIGN, "q must be 16-byte aligned with ld_q %% 16 == 0");
+    REQUIRE(aligned16(s), BS_ERR_ALIGN, "s must be 16-byte aligned");
+    if (G == 0 || R == 0 || C == 0) return ok();
+    bs::Quant128Args a{x, G, R, C, stride_xg, ld_x, q, stride_qg, ld_q, s, stride_sg, ld_s, R / 128, C / 128};
+    return hip_status(bs::launch_quant_128x128(a, true, stream), fn);
+}
+
+namespace {
+
+bs_status check_gemm_common(const char* fn, int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
+                            const float* sa, int64_t ld_sa, const uint8_t* b, int64_t ldb, const float* sb,
+                            int64_t ld_sb, bs_scale_kind b_kind, void* d, int64_t ldd, bs_dtype d_dtype) {
+    REQUIRE((a && sa) || M == 0 || K == 0, BS_ERR_NULL, "a and sa must be non-NULL");
+    REQUIRE((b && sb) || N == 0 || K == 0, BS_ERR_NULL, "b and sb must be non-NULL");
+    REQUIRE(d || M == 0 || N == 0, BS_ERR_NULL, "d must be non-NULL");
+    REQUIRE(b_kind == BS_SCALE_1X128 || b_kind == BS_SCALE_128X128, BS_ERR_MODE,
+            "b_kind=%d must be BS_SCALE_1X128 (4) or BS_SCALE_128X128 (5)", (int)b_kind);
+    REQUIRE(d_dtype == BS_OUT_BF16 || d_dtype == BS_OUT_F32, BS_ERR_MODE, "d_dtype=%d must be BF16 or F32",
+            (int)d_dtype);
+    REQUIRE(M >= 0 && N >= 0 && K >= 0, BS_ERR_SHAPE, "M, N, K must be >= 0");
+    REQUIRE(N % 128 == 0, BS_ERR_SHAPE, "N=%lld must be a multiple of 128", (long long)N);
+    REQUIRE(K % 128 == 0, BS_ERR_SHAPE, "K=%lld must be a multiple of 128 (1x128 blocks along K)", (long long)K);
+    REQUIRE(lda >= K, BS_ERR_LAYOUT,
+            "lda=%lld < K=%lld: a must be row-major [M, K] (contiguous along the contraction)", (long long)lda,
+            (long long)K);
+    REQUIRE(ldb >= K, BS_ERR_LAYOUT,
+            "ldb=%lld < K=%lld: b must be [N, K] contiguous along K (column-major B of D = A.B)", (long long)ldb,
+            (long long)K);
+    REQUIRE(ldd >= N, BS_ERR_LAYOUT, "ldd=%lld < N=%lld: d is row-major [M, N]", (long long)ldd, (long long)N);
+    REQUIRE(ld_sa % 4 == 0, BS_ERR_LAYOUT, "ld_sa=%lld must be a multiple of 4", (long long)ld_sa);
+    REQUIRE(ld_sb % 4 == 0, BS_ERR_LAYOUT, "ld_sb=%lld must be a multiple of 4", (long long)ld_sb);
+    // Operand tiles and scale rows are addressed with 32-bit buffer offsets.
+    REQUIRE(lda < (1ll << 23) && ldb < (1ll << 23), BS_ERR_LAYOUT,
+            "lda and ldb must be < 2^23 elements (32-bit tile offsets)");
+    REQUIRE((K / 128 + 1) * (ld_sa > ld_sb ? ld_sa : ld_sb) < (1ll << 29), BS_ERR_LAYOUT,
+            "scale tensors must be smaller than 2 GiB (32-bit offsets)");
+    REQUIRE(aligned16(a) && lda % 16 == 0, BS_ERR_ALIGN, "a must be 16-byte aligned with lda %% 16 == 0");
+    REQUIRE(aligned16(b) && ldb % 16 == 0, BS_ERR_ALIGN, "b must be 16-byte aligned with ldb %% 16 == 0");
+    REQUIRE(aligned16(sa) && aligned16(sb), BS_ERR_ALIGN, "sa and sb must be 16-byte aligned");
+    REQUIRE(aligned16(d) && ldd % (d_dtype == BS_OUT_F32 ? 4 : 8) == 0, BS_ERR_ALIGN,
+            "d must be 16-byte aligned with 16-byte rows");
+    return ok();
+}
+
+}  // namespace
+
+bs_status bs_scaled_mm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const float* sa,
+                       int64_t ld_sa, bs_scale_kind a_kind, const uint8_t* b, int64_t ldb, const float* sb,
+                       int64_t ld_sb, bs_scale_kind b_kind, void* d, int64_t ldd, bs_dtype d_dtype,
+                       hipStream_t stream) {
+    static const char* fn = "bs_scaled_mm";
+    REQUIRE(a_kind == BS_SCALE_1X128, BS_ERR_MODE, "a_kind=%d: A takes 1x128 scales (BS_SCALE_1X128 = 4)",
+            (int)a_kind);
+    bs_status st = check_gemm_common(fn, M, N, K, a, lda, sa, ld_sa, b, ldb, sb, ld_sb, b_kind, d, ldd, d_dtype);
+    if (st != BS_OK) return st;
+    REQUIRE(ld_sa >= M, BS_ERR_LAYOUT, "ld_sa=%lld < M=%lld: sa is K-major [K/128][ld_sa >= M]",
+            (long long)ld_sa, (long long)M);
+    const int64_t nrows_sb = b_kind == BS_SCALE_1X128 ? N : N / 128;
+    REQUIRE(ld_sb >= nrows_sb, BS_ERR_LAYOUT, "ld_sb=%lld < %lld: sb is K-major [K/128][ld_sb >= %s]",
+            (long long)ld_sb, (long long)nrows_sb, b_kind == BS_SCALE_1X128 ? "N" : "N/128");
+    if (M == 0 || N == 0) return ok();
+    bs::GemmArgs g{};
+    g.M = M; g.N = N; g.K = K;
+    g.a = a; g.lda = lda; g.sa = sa; g.ld_sa = ld_sa;
+    g.b = b; g.ldb = ldb; g.sb = sb; g.ld_sb = ld_sb;
+    g.d = d; g.ldd = ldd;
+    g.G = 1;
+    g.tiles_m = (M + 255) / 256;
+    g.tiles_n = (N + 255) / 256;
+    g.num_tiles = g.tiles_m * g.tiles_n;
+    return hip_status(bs::launch_gemm(g, bs::kDense, b_kind == BS_SCALE_1X128, d_dtype == BS_OUT_F32, stream), fn);
+}
+
+bs_status bs_grouped_scaled_mm(bs_group_mode mode, int64_t G, int64_t M, int64_t N, int64_t K,
+                               const int32_t* group_end, const uint8_t* a, int64_t lda, const float* sa,
+                               int64_t ld_sa, const uint8_t* b, int64_t stride_bg, int64_t ldb, const float* sb,
+                               int64_t stride_sbg, int64_t ld_sb, bs_scale_kind b_kind, void* d, int64_t stride_dg,
+                               int64_t ldd, bs_dtype d_dtype, hipStream_t stream) {
+    static const char* fn = "bs_grouped_scaled_mm";
+    REQUIRE(mode == BS_GROUP_M || mode == BS_GROUP_K, BS_ERR_MODE, "mode=%d must be BS_GROUP_M or BS_GROUP_K",
+            (int)mode);
+    REQUIRE(group_end, BS_ERR_NULL, "group_end is NULL");
+    REQUIRE(G >= 0, BS_ERR_SHAPE, "G=%lld must be >= 0", (long long)G);
+    bs_status st = check_gemm_common(fn, M, N, K, a, lda, sa, ld_sa, b, ldb, sb, ld_sb, b_kind, d, ldd, d_dtype);
+    if (st != BS_OK) return st;
+    REQUIRE(ld_sa >= M, BS_ERR_LAYOUT, "ld_sa=%lld < M=%lld: sa is K-major [K/128][ld_sa >= M]",
+            (long long)ld_sa, (long long)M);
+    bs::GemmArgs g{};
+    g.M = M; g.N = N; g.K = K;
+    g.a = a; g.lda = lda; g.sa = sa; g.ld_sa = ld_sa;
+    g.b = b; g.ldb = ldb; g.sb = sb; g.ld_sb = ld_sb;
+    g.d = d; g.ldd = ldd;
+    g.G = G; g.group_end = group_end;
+    g.tiles_n = (N + 255) / 256;
+    if (mode == BS_GROUP_M) {
+        REQUIRE(b_kind == BS_SCALE_128X128, BS_ERR_MODE,
+                "BS_GROUP_M takes 128x128 expert-weight scales (b_kind = BS_SCALE_128X128)");
+        REQUIRE(stride_dg == 0, BS_ERR_MODE, "BS_GROUP_M writes one D [M, N]: stride_dg must be 0");
+        REQUIRE(ld_sb >= N / 128, BS_ERR_LAYOUT, "ld_sb=%lld < N/128: sb[g] is K-major [K/128][ld_sb >= N/128]",
+                (long long)ld_sb);
+        // Expert operands are inputs: their regions may interleave (e.g. the
+        // scales of W quantized as one [G*N, K] matrix, stride_sbg = N/128).
+        REQUIRE(stride_bg >= 0 && stride_sbg >= 0, BS_ERR_LAYOUT, "stride_bg and stride_sbg must be >= 0");
+        REQUIRE(stride_bg % 16 == 0, BS_ERR_ALIGN, "stride_bg must be a multiple of 16 bytes");
+        if (G == 0 || M == 0 || N == 0) return ok();
+        g.stride_bg = stride_bg;
+        g.stride_sbg = stride_sbg;
+        g.tiles_m = (M + 255) / 256;
+        g.num_tiles = (g.tiles_m + G) * g.tiles_n;  // upper bound on the sum of per-group tile rows
+        return hip_status(bs::launch_gemm(g, bs::kGroupM, false, d_dtype == BS_OUT_F32, stream), fn);
+    }
+    REQUIRE(b_kind == BS_SCALE_1X128, BS_ERR_MODE,
+            "BS_GROUP_K contracts two 1x128-scaled operands (b_kind = BS_SCALE_1X128)");
+    REQUIRE(stride_bg == 0 && stride_sbg == 0, BS_ERR_MODE,
+            "BS_GROUP_K shares one B over the groups: stride_bg and stride_sbg must be 0");
+    REQUIRE(M % 128 == 0, BS_ERR_SHAPE, "M=%lld must be a multiple of 128 for BS_GROUP_K", (long long)M);
+    REQUIRE(ld_sb >= N, BS_ERR_LAYOUT, "ld_sb=%lld < N=%lld: sb is K-major [K/128][ld_sb >= N]", (long long)ld_sb,
+            (long long)N);
+    REQUIRE(G <= 1 || stride_dg >= M * ldd, BS_ERR_LAYOUT, "stride_dg=%lld < M*ldd", (long long)stride_dg);
+    REQUIRE(stride_dg % (d_dtype == BS_OUT_F32 ? 4 : 8) == 0, BS_ERR_ALIGN,
+            "stride_dg must keep every D[g] 16-byte aligned");
+    if (G == 0 || M == 0 || N == 0) return ok();
+    g.stride_dg = stride_dg;
+    g.tiles_m = (M + 255) / 256;
+    g.num_tiles = G * g.tiles_m * g.tiles_n;
+    return hip_status(bs::launch_gemm(g, bs::kGroupK, true, d_dtype == BS_OUT_F32, stream), fn);
+}
+
+bs_status bs_diag_e4m3_census(uint32_t* min_bits, uint32_t* max_bits, unsigned long long* counts,
+                              hipStream_t stream) {
+    static const char* fn = "bs_diag_e4m3_census";
+    REQUIRE(min_bits && max_bits && counts, BS_ERR_NULL, "outputs must be non-NULL");
+    return hip_status(bs::launch_diag_e4m3_census(min_bits, max_bits, counts, stream), fn);
+}
+
+bs_status bs_diag_division(unsigned long long* result, hipStream_t stream) {
+    static const char* fn = "bs_diag_division";
+    REQUIRE(result, BS_ERR_NULL, "result must be non-NULL");
+    return hip_status(bs::launch_diag_division(result, stream), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Internal interface between the C ABI layer (bs_api.hip) and the kernel
+// translation units.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bs {
+
+struct Quant1x128Args {
+    const uint16_t* x;
+    int64_t R, C, ld_x;
+    uint8_t* q_row;
+    int64_t ld_qr;
+    float* s_row;
+    int64_t ld_sr;
+    uint8_t* q_col;
+    int64_t ld_qc;
+    float* s_col;
+    int64_t ld_sc;
+    int64_t col_tiles;  // C / 128
+};
+
+struct Quant128Args {
+    const uint16_t* x;
+    int64_t G, R, C, stride_xg, ld_x;
+    uint8_t* q;
+    int64_t stride_qg, ld_q;
+    float* s;
+    int64_t stride_sg, ld_s;
+    int64_t row_tiles, col_tiles;  // R / 128, C / 128
+};
+
+enum GroupKind { kDense = 0, kGroupM = 1, kGroupK = 2 };
+
+struct GemmArgs {
+    int64_t M, N, K;
+    const uint8_t* a;
+    int64_t lda;
+    const float* sa;
+    int64_t ld_sa;
+    const uint8_t* b;
+    int64_t ldb;
+    const float* sb;
+    int64_t ld_sb;
+    void* d;
+    int64_t ldd;
+    // grouped forms
+    int64_t G;
+    const int32_t* group_end;
+    int64_t stride_bg, stride_sbg, stride_dg;
+    // launch geometry
+    int64_t tiles_m, tiles_n;  // tiles of the dense problem (GROUP_K: per group)
+    int64_t num_tiles;         // grid size (an upper bound for GROUP_M)
+};
+
+hipError_t launch_quant_1x128(const Quant1x128Args& a, bool row, bool col, hipStream_t stream);
+hipError_t launch_quant_128x128(const Quant128Args& a, bool transpose, hipStream_t stream);
+
+// b_1x128: B scales per row (wgrad) instead of per 128x128 block.
+hipError_t launch_gemm(const GemmArgs& a, GroupKind kind, bool b_1x128, bool out_f32, hipStream_t stream);
+
+hipError_t launch_diag_e4m3_census(uint32_t* min_bits, uint32_t* max_bits, unsigned long long* counts,
+                                   hipStream_t stream);
+hipError_t launch_diag_division(unsigned long long* result, hipStream_t stream);
+
+}  // namespace bs

@@ -1,0 +1,257 @@
+/*
+ * bs.h -- C ABI of the blockwise-scaled FP8 training kernels for AMD gfx950.
+ *
+ * The method (pages: "[not for land] float8 blockwise scaling training
+ * prototype using deep_gemm", description; "[mxfp8 moe training] use new 3d
+ * colwise quantization kernel", summary; "add FSDP and TP tests for
+ * Float8BlockwiseLinear", summary and review threads):
+ *
+ *   - activations and gradients are quantized to e4m3 with one fp32 scale
+ *     per 1x128 block along the GEMM contraction dimension;
+ *   - weights are quantized with one fp32 scale per 128x128 block;
+ *   - a scaled GEMM multiplies the e4m3 codes on the matrix cores and applies
+ *     the two block scales of every 128-wide contraction block to the fp32
+ *     partial sum before adding it to an fp32 accumulator;
+ *   - forward out = A.W^T, dgrad grad_in = grad_out.W, wgrad
+ *     grad_W = grad_out^T.A (both operands 1x128 along the token axis), and a
+ *     grouped (MoE) form of each, with the expert weights quantized
+ *     column-wise in 3-D for the backward.
+ *
+ * Quantization of one block x (bf16 values):
+ *     amax = max|x|;  s = fl32(max(amax, EPS) / 448);  EPS = fl32(1e-12)
+ *     q    = e4m3_rne(clamp(fl32(x / s), -448, 448))      (sign of zero kept)
+ * e4m3 is the OCP FP8 E4M3 encoding (bias 7, max 448, NaN 0x7F/0xFF, no Inf).
+ * Inputs must be finite; the result for Inf/NaN inputs is unspecified.
+ *
+ * Conventions for every entry point
+ *   - Dimensions and leading dimensions ("ld") are in ELEMENTS, int64_t.
+ *   - bf16 tensors are passed as uint16_t bit patterns, e4m3 codes as uint8_t,
+ *     scales as float.  All data pointers are DEVICE pointers.  A pointer may
+ *     be NULL only when the tensor it points to has no elements.
+ *   - Matrices are row-major with unit stride along the last dimension:
+ *     element (i, j) of X is X[i * ld + j].  Both GEMM operands are
+ *     contiguous along the contraction dimension ("A row-major, B
+ *     column-major", "add FSDP and TP tests for Float8BlockwiseLinear",
+ *     review thread on the layout assertions).
+ *   - Scales are "K-major" (same page, review thread on
+ *     _pad_blockwise_128x128_scale_k_major): the contraction-block index is
+ *     the outer index and the row (1x128) or row-block (128x128) index is
+ *     contiguous, s[kb * ld_s + row] or s[kb * ld_s + row / 128], and ld_s is
+ *     a multiple of 4 (16 bytes).  One layout serves every scale tensor.
+ *     Scale padding entries (index >= the logical count) are never written.
+ *   - Ownership: the caller owns every buffer.  The library allocates nothing,
+ *     keeps no state between calls and is thread-safe.  Outputs must not
+ *     alias inputs or each other.
+ *   - Execution: every call validates its arguments on the host, then
+ *     enqueues its kernels on `stream` (NULL = the default stream) and returns
+ *     without synchronizing.  Nothing is enqueued when validation fails.
+ *   - Errors: a nonzero bs_status; bs_last_error() returns a message for the
+ *     calling thread that names the argument and the required layout.  A
+ *     kernel launch failure returns BS_ERR_HIP.
+ *   - Alignment: data pointers must be 16-byte aligned and leading dimensions
+ *     must make every row start 16-byte aligned (bf16: ld % 8 == 0, e4m3:
+ *     ld % 16 == 0, fp32: ld % 4 == 0).
+ */
+#ifndef BS_H
+#define BS_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bs_status {
+    BS_OK = 0,
+    BS_ERR_NULL = 1,    /* a required pointer is NULL                        */
+    BS_ERR_SHAPE = 2,   /* a blocked dimension is not a multiple of 128, or <0 */
+    BS_ERR_LAYOUT = 3,  /* a leading dimension / group stride is too small,
+                           or a scale ld is not a multiple of 4              */
+    BS_ERR_ALIGN = 4,   /* a pointer or row is not 16-byte aligned           */
+    BS_ERR_MODE = 5,    /* unsupported scale kind, dtype or group mode       */
+    BS_ERR_HIP = 6      /* the HIP runtime rejected a launch                 */
+} bs_status;
+
+/* Scale recipes.  The numbers are those of the recipe enum the pages use
+ * ("add FSDP and TP tests for Float8BlockwiseLinear", review thread on
+ * _SCALING_TYPE: BlockWise1x128 is 4, and 5 is the 128x128 recipe). */
+typedef enum bs_scale_kind {
+    BS_SCALE_1X128 = 4,
+    BS_SCALE_128X128 = 5
+} bs_scale_kind;
+
+typedef enum bs_dtype {
+    BS_OUT_BF16 = 0,    /* output rounded to bf16, nearest-even              */
+    BS_OUT_F32 = 1
+} bs_dtype;
+
+typedef enum bs_group_mode {
+    BS_GROUP_M = 0,     /* groups of rows of A, one B per group (MoE fwd/dgrad) */
+    BS_GROUP_K = 1      /* groups along the contraction, one D per group (wgrad) */
+} bs_group_mode;
+
+/*
+ * bs_quant_1x128 -- 1x128 quantizer of activations / gradients, one HBM pass
+ * producing either or both of
+ *   row output: blocks of 128 consecutive elements of a row of X
+ *               q_row[r * ld_qr + c],  s_row[(c / 128) * ld_sr + r]
+ *   col output: blocks of 128 consecutive rows of a column of X, written
+ *               transposed so that the token axis is contiguous:
+ *               q_col[c * ld_qc + r] (code of X[r][c]),
+ *               s_col[(r / 128) * ld_sc + c]
+ * The row output is the A operand of the forward (activations) and dgrad
+ * (grad_out) GEMMs; the col output is an operand of the wgrad GEMM.
+ * Pages: "[not for land] float8 blockwise scaling training prototype using
+ * deep_gemm", description (1x128 activation scaling; the grad_weight GEMM).
+ *
+ *   x      [R, C] bf16, ld_x >= C.  C % 128 == 0.  R >= 0; R % 128 == 0 when
+ *          the col output is requested (a ragged R is allowed for rows only).
+ *   q_row, s_row   both NULL or both set.  ld_qr >= C, ld_sr >= R.
+ *   q_col, s_col   both NULL or both set.  ld_qc >= R, ld_sc >= C.
+ *   At least one output pair must be set.
+ */
+bs_status bs_quant_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x,
+                         uint8_t* q_row, int64_t ld_qr, float* s_row, int64_t ld_sr,
+                         uint8_t* q_col, int64_t ld_qc, float* s_col, int64_t ld_sc,
+                         hipStream_t stream);
+
+/*
+ * bs_quant_128x128 -- weight quantizer, one scale per 128x128 tile.
+ *   x [R, C] bf16 (R = out features, C = in features = contraction),
+ *   q[r * ld_q + c], s[(c / 128) * ld_s + r / 128].
+ *   R % 128 == 0, C % 128 == 0, ld_x >= C, ld_q >= C, ld_s >= R / 128.
+ * Pages: prototype page, description ("128x128 scaling of a single tensor ...
+ * 3 kernels per tensor"; "a fast version of 128x128 scaling ... with a
+ * handwritten kernel"); "add FSDP and TP tests ...", review thread on the
+ * K-major scale padding.
+ */
+bs_status bs_quant_128x128(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x,
+                           uint8_t* q, int64_t ld_q, float* s, int64_t ld_s,
+                           hipStream_t stream);
+
+/*
+ * bs_quant_3d_colwise -- expert weights W[G][R][C] quantized in 128x128
+ * tiles and written transposed, giving the contraction-contiguous operand of
+ * the dgrad GEMM (grad_in = grad_out . W) for every expert:
+ *   q[g * stride_qg + c * ld_q + r]   = code of W[g][r][c]
+ *   s[g * stride_sg + (r / 128) * ld_s + c / 128] = scale of tile (r/128, c/128)
+ * (the scale index is K-major for the transposed operand, whose contraction
+ * is r).  G >= 0, R % 128 == 0, C % 128 == 0; ld_x >= C, stride_xg >= R*ld_x;
+ * ld_q >= R, stride_qg >= C*ld_q; ld_s >= C/128, stride_sg >= (R/128)*ld_s,
+ * stride_sg % 4 == 0.  G = 1 is the dense linear's transposed weight.
+ * Pages: "[mxfp8 moe training] use new 3d colwise quantization kernel",
+ * summary (a kernel that quantizes a 3-D expert-weight tensor column-wise for
+ * the scaled grouped GEMM backward).  The pages give that kernel for another
+ * block format; the 128x128 tile here is this library's reading for the
+ * 128x128 weight recipe.
+ */
+bs_status bs_quant_3d_colwise(const uint16_t* x, int64_t G, int64_t R, int64_t C,
+                              int64_t stride_xg, int64_t ld_x,
+                              uint8_t* q, int64_t stride_qg, int64_t ld_q,
+                              float* s, int64_t stride_sg, int64_t ld_s,
+                              hipStream_t stream);
+
+/*
+ * bs_scaled_mm -- D[M, N] = sum_kb sa(m, kb) * sb(n, kb) * P_kb[m, n],
+ * P_kb = sum over k in block kb of dec(a[m][k]) * dec(b[n][k]) (fp32 MFMA),
+ * accumulated in fp32 and written as bf16 (nearest-even) or fp32.
+ * Pages: "add FSDP and TP tests for Float8BlockwiseLinear", summary and review
+ * threads (blockwise_scaled_mm(a, scale_a, scale_recipe_a, b, scale_b,
+ * scale_recipe_b); one scale layout; fail loudly on wrong layouts);
+ * prototype page, description (fwd and bwd GEMMs of a dense linear; the
+ * "1x128 by 1x128" grad_weight GEMM).
+ *
+ *   a  [M, K] e4m3, lda >= K;  sa 1x128: sa[(k/128) * ld_sa + m], ld_sa >= M.
+ *      a_kind must be BS_SCALE_1X128.
+ *   b  [N, K] e4m3, ldb >= K;
+ *      b_kind BS_SCALE_128X128: sb[(k/128) * ld_sb + n/128], ld_sb >= ceil(N/128),
+ *             N % 128 == 0  (forward: b = W; dgrad: b = W^T from
+ *             bs_quant_3d_colwise with G = 1)
+ *      b_kind BS_SCALE_1X128:  sb[(k/128) * ld_sb + n],      ld_sb >= N
+ *             (wgrad: a = grad_out^T, b = A^T, both from the col output of
+ *             bs_quant_1x128)
+ *   d  [M, N], ldd >= N, d_dtype BS_OUT_BF16 (uint16 bits) or BS_OUT_F32.
+ *   M >= 0 (any), N % 128 == 0, K % 128 == 0.  K == 0 writes zeros.
+ */
+bs_status bs_scaled_mm(int64_t M, int64_t N, int64_t K,
+                       const uint8_t* a, int64_t lda, const float* sa, int64_t ld_sa,
+                       bs_scale_kind a_kind,
+                       const uint8_t* b, int64_t ldb, const float* sb, int64_t ld_sb,
+                       bs_scale_kind b_kind,
+                       void* d, int64_t ldd, bs_dtype d_dtype,
+                       hipStream_t stream);
+
+/*
+ * bs_grouped_scaled_mm -- the MoE form of bs_scaled_mm (pages: prototype page,
+ * description, "fwd and bwd grouped gemms for MoE"; "[mxfp8 moe training]
+ * ...", microbenchmark table, shapes (M, N, K, G)).
+ *
+ * group_end: DEVICE int32[G], cumulative ends of the G groups along the
+ * grouped axis, non-decreasing, last == the axis length; zero-size groups are
+ * allowed.  Read on the device (no host synchronization).  Kernels clamp
+ * every end into [0, axis length] and treat a decreasing end as an empty
+ * group, so malformed ends can never cause an out-of-bounds access.
+ *
+ *   BS_GROUP_M (forward, dgrad): rows [end_{g-1}, end_g) of A use expert g:
+ *     a [M, K] 1x128 scales as in bs_scaled_mm; b_kind BS_SCALE_128X128;
+ *     expert g's B is b + g*stride_bg ([N, K], ldb) with scales
+ *     sb + g*stride_sbg (sb[(k/128)*ld_sb + n/128]);  d [M, N], ldd;
+ *     stride_dg must be 0.  Rows past the last end are not written.
+ *   BS_GROUP_K (wgrad): contraction groups; the ends must be multiples of 128:
+ *     a [M, K] and b [N, K] both with 1x128 scales along K (sa[(k/128)*ld_sa + m],
+ *     sb[(k/128)*ld_sb + n]); b_kind BS_SCALE_1X128; stride_bg and stride_sbg
+ *     must be 0; expert g's result is d + g*stride_dg ([M, N], ldd),
+ *     D_g = sum over k in [end_{g-1}, end_g); an empty group writes zeros.
+ *   M >= 0 (GROUP_M) or M % 128 == 0 (GROUP_K); N % 128 == 0; K % 128 == 0.
+ */
+bs_status bs_grouped_scaled_mm(bs_group_mode mode, int64_t G, int64_t M, int64_t N, int64_t K,
+                               const int32_t* group_end,
+                               const uint8_t* a, int64_t lda, const float* sa, int64_t ld_sa,
+                               const uint8_t* b, int64_t stride_bg, int64_t ldb,
+                               const float* sb, int64_t stride_sbg, int64_t ld_sb,
+                               bs_scale_kind b_kind,
+                               void* d, int64_t stride_dg, int64_t ldd, bs_dtype d_dtype,
+                               hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* bs_status_string(bs_status status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* bs_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Diagnostics: exhaustive self-checks of the quantizers' arithmetic.  They
+ * run the same device routines as the quantizer kernels.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * bs_diag_e4m3_census -- applies the quantizers' final step (clamp to
+ * [-448, 448], then round to e4m3) to EVERY float32 value y with |y| <= 448
+ * of both signs and records, per output code c (0..255), the smallest and
+ * largest |y| bit pattern (sign bit cleared) that produced it and how many
+ * did.  Outputs: device uint32 min_bits[256], max_bits[256], uint64
+ * counts[256]; codes never produced have count 0.  Monotone rounding gives
+ * max_bits - min_bits + 1 == count for every produced code.
+ */
+bs_status bs_diag_e4m3_census(uint32_t* min_bits, uint32_t* max_bits,
+                              unsigned long long* counts, hipStream_t stream);
+
+/*
+ * bs_diag_division -- checks the quantizers' element division fl32(x / s)
+ * against the correctly rounded IEEE division for every pair reachable from
+ * bf16 inputs: s = fl32(max(amax, EPS) / 448) for every finite bf16 amax
+ * >= 0 (amax = 0 takes the EPS floor), and every finite bf16 x of either
+ * sign with |x| <= max(amax, EPS).  Output: device uint64 result[5] =
+ * {pairs checked, scale mismatches, e4m3 code mismatches, quotient
+ * mismatches with |x/s| >= 2^-10, quotient mismatches with |x/s| < 2^-10}.
+ * The last count is informational: such quotients encode to a zero of the
+ * quotient's sign whatever their low bits.
+ */
+bs_status bs_diag_division(unsigned long long* result, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BS_H */

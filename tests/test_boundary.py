@@ -1,0 +1,155 @@
+"""C-ABI boundary checks that need no GPU.
+
+The library must load, export every function declared in include/bs.h, and
+reject malformed arguments on the host with the documented status code and a
+message naming the layout -- before anything is enqueued.  The pointers here
+are fake (never dereferenced: validation fails first).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from blockwise_scaled_fp8_bs_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bs.h")
+
+OK, NULL, SHAPE, LAYOUT, ALIGN, MODE = 0, 1, 2, 3, 4, 5
+P = 0x10000  # a fake 16-byte aligned address
+PU = 0x10004  # a fake misaligned address
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:bs_status|const char\*)\s+(bs_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libbs.so is not built (python -m blockwise_scaled_fp8_bs_amd.build)")
+    return _lib.load()
+
+
+def test_header_declares_the_five_entry_points():
+    names = declared_functions()
+    for n in ["bs_quant_1x128", "bs_quant_128x128", "bs_quant_3d_colwise", "bs_scaled_mm",
+              "bs_grouped_scaled_mm", "bs_status_string", "bs_last_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, f"binding lacks a signature for {name}"
+
+
+def test_status_strings(lib):
+    assert lib.bs_status_string(0) == b"BS_OK"
+    assert lib.bs_status_string(3) == b"BS_ERR_LAYOUT"
+    assert lib.bs_status_string(99) == b"BS_ERR_UNKNOWN"
+
+
+def _q1(lib, x=P, R=256, C=512, ld_x=512, q_row=P, ld_qr=512, s_row=P, ld_sr=256, q_col=None, ld_qc=0,
+        s_col=None, ld_sc=0):
+    return lib.bs_quant_1x128(x, R, C, ld_x, q_row, ld_qr, s_row, ld_sr, q_col, ld_qc, s_col, ld_sc, None)
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(x=None), NULL, "x is NULL"),
+    (dict(q_row=None), NULL, "both"),
+    (dict(q_row=None, s_row=None), NULL, "no output"),
+    (dict(C=500, ld_x=512, ld_qr=512), SHAPE, "multiple of 128"),
+    (dict(R=-1), SHAPE, ">= 0"),
+    (dict(ld_x=256), LAYOUT, "row-major"),
+    (dict(ld_sr=200), LAYOUT, "K-major"),
+    (dict(ld_sr=258), LAYOUT, "multiple of 4"),
+    (dict(x=PU), ALIGN, "aligned"),
+    (dict(ld_qr=520), ALIGN, "ld_qr"),
+    (dict(R=200, q_col=P, ld_qc=256, s_col=P, ld_sc=512), SHAPE, "column output"),
+    (dict(q_col=P, ld_qc=100, s_col=P, ld_sc=512), LAYOUT, "transpose"),
+])
+def test_quant_1x128_validation(lib, kw, code, frag):
+    assert _q1(lib, **kw) == code
+    assert frag in lib.bs_last_error().decode()
+
+
+def test_quant_1x128_empty_is_ok_without_launch(lib):
+    assert _q1(lib, R=0) == OK
+    assert lib.bs_last_error() == b""
+
+
+def test_quant_128x128_validation(lib):
+    f = lib.bs_quant_128x128
+    assert f(P, 200, 512, 512, P, 512, P, 4, None) == SHAPE
+    assert f(P, 256, 512, 512, P, 512, P, 1, None) == LAYOUT
+    assert "K-major" in lib.bs_last_error().decode()
+    assert f(P, 256, 512, 512, P, 512, P, 6, None) == LAYOUT
+    assert "multiple of 4" in lib.bs_last_error().decode()
+    assert f(P, 0, 512, 512, P, 512, P, 4, None) == OK
+
+
+def test_quant_3d_colwise_validation(lib):
+    f = lib.bs_quant_3d_colwise
+    # G=2, R=256, C=384: q[g] is [384, 256]
+    assert f(P, 2, 256, 384, 256 * 384, 384, P, 384 * 256, 100, P, 8, 4, None) == LAYOUT  # ld_q < R
+    assert f(P, 2, 256, 384, 100, 384, P, 384 * 256, 256, P, 8, 4, None) == LAYOUT       # stride_xg
+    assert f(P, 2, 256, 384, 256 * 384, 384, P, 384 * 256, 256, P, 4, 4, None) == LAYOUT  # stride_sg
+    assert f(P, 0, 256, 384, 0, 384, P, 0, 256, P, 0, 4, None) == OK
+
+
+def _mm(lib, M=256, N=256, K=512, a=P, lda=512, sa=P, ld_sa=256, a_kind=4, b=P, ldb=512, sb=P, ld_sb=4,
+        b_kind=5, d=P, ldd=256, dt=0):
+    return lib.bs_scaled_mm(M, N, K, a, lda, sa, ld_sa, a_kind, b, ldb, sb, ld_sb, b_kind, d, ldd, dt, None)
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(a=None), NULL, "non-NULL"),
+    (dict(d=None), NULL, "d must be"),
+    (dict(a_kind=5), MODE, "a_kind"),
+    (dict(b_kind=7), MODE, "b_kind"),
+    (dict(dt=3), MODE, "d_dtype"),
+    (dict(K=500, lda=512, ldb=512), SHAPE, "multiple of 128"),
+    (dict(N=200, ldd=256), SHAPE, "N=200"),
+    (dict(lda=256), LAYOUT, "row-major [M, K]"),
+    (dict(ldb=256), LAYOUT, "column-major"),
+    (dict(ldd=128), LAYOUT, "row-major [M, N]"),
+    (dict(ld_sa=128), LAYOUT, "K-major"),
+    (dict(ld_sb=2), LAYOUT, "multiple of 4"),
+    (dict(b_kind=4, ld_sb=4), LAYOUT, "ld_sb >= N"),
+    (dict(a=PU), ALIGN, "aligned"),
+    (dict(ldd=260), ALIGN, "16-byte rows"),
+])
+def test_scaled_mm_validation(lib, kw, code, frag):
+    assert _mm(lib, **kw) == code
+    assert frag in lib.bs_last_error().decode()
+
+
+def test_scaled_mm_empty_is_ok(lib):
+    assert _mm(lib, M=0) == OK
+
+
+def test_grouped_validation(lib):
+    f = lib.bs_grouped_scaled_mm
+    base = dict(mode=0, G=2, M=256, N=256, K=512, ge=P, a=P, lda=512, sa=P, ld_sa=256, b=P, sbg=256 * 512,
+                ldb=512, sb=P, ssbg=2, ld_sb=4, b_kind=5, d=P, sdg=0, ldd=256, dt=0)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["mode"], a["G"], a["M"], a["N"], a["K"], a["ge"], a["a"], a["lda"], a["sa"], a["ld_sa"],
+                 a["b"], a["sbg"], a["ldb"], a["sb"], a["ssbg"], a["ld_sb"], a["b_kind"], a["d"], a["sdg"],
+                 a["ldd"], a["dt"], None)
+
+    assert call(mode=2) == MODE
+    assert call(ge=None) == NULL
+    assert call(b_kind=4) == MODE
+    assert call(sdg=5) == MODE
+    assert call(G=0) == OK
+    # GROUP_K
+    assert call(mode=1, b_kind=5) == MODE
+    assert call(mode=1, b_kind=4, ld_sb=256, sbg=0, ssbg=0, sdg=10) == LAYOUT
+    assert call(mode=1, b_kind=4, ld_sb=256, sbg=0, ssbg=0, sdg=256 * 256, G=0) == OK
+    assert call(mode=1, b_kind=4, ld_sb=256, sbg=7, ssbg=0, sdg=256 * 256) == MODE

@@ -1,0 +1,214 @@
+"""GPU parity of the scaled GEMMs (dense and grouped) against the CPU oracle.
+
+Operand codes and scales are made on the CPU by the oracle's quantizer (or
+drawn directly), copied to the GPU in the library's layout, and the GPU
+result is compared element by element with the oracle's float64 product
+within 2e-3 * ||a_m|| * ||b_n||; exact-arithmetic cases must match bit for
+bit.  Calls go through the C ABI (thin binding)."""
+
+import numpy as np
+import pytest
+import torch
+
+import blockwise_scaled_fp8_bs_amd as bs
+from blockwise_scaled_fp8_bs_amd import inputs
+from oracle import e4m3, gemm, quant
+from gpu_support import bits16, check_canaries, guarded, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def to_gpu_scales(s_logical, pad=4):
+    """Logical [rows, nkb] scales -> K-major GPU tensor [nkb, roundup4(rows) + pad]."""
+    rows, nkb = s_logical.shape
+    ld = (rows + 3) // 4 * 4 + pad
+    buf = np.full((nkb, ld), np.nan, dtype=np.float32)
+    buf[:, :rows] = s_logical.T
+    return torch.from_numpy(buf).cuda()
+
+
+def operand_1x128(rows, K, sigma, seed):
+    x = inputs.bf16_normal((rows, K), sigma, seed)
+    return quant.quant_1x128_rowwise(bits16(x))
+
+
+def operand_128x128(rows, K, sigma, seed):
+    x = inputs.bf16_normal((rows, K), sigma, seed)
+    return quant.quant_128x128(bits16(x))
+
+
+def check_result(d_gpu, qa, sa, qb, sb, b_row_block, exact=False):
+    a = gemm.dequant(qa, sa, 1)
+    b = gemm.dequant(qb, sb, b_row_block)
+    ref = a @ b.T
+    d = d_gpu.float().cpu().numpy().astype(np.float64)
+    if exact:
+        bad = np.argwhere(d != ref)
+        assert bad.size == 0, f"{len(bad)} inexact elements, first {bad[0]}: {d[tuple(bad[0])]} vs {ref[tuple(bad[0])]}"
+    else:
+        ok, worst = gemm.check_close(d, ref, a, b)
+        assert ok, f"worst |err| / bound = {worst}"
+    return ref
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 512), (384, 640, 768), (300, 384, 512), (512, 128, 1024),
+                                   (64, 256, 128)])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_scaled_mm_128x128(M, N, K, out_dtype):
+    need_gpu()
+    qa, sa = operand_1x128(M, K, 1.0, seed=M + K)
+    qb, sb = operand_128x128(N, K, 0.02, seed=N + 3 * K)
+    full, out = guarded(M, N, out_dtype)
+    print(f"scaled_mm 128x128 M={M} N={N} K={K} {out_dtype}", flush=True)
+    bs.bs_scaled_mm(torch.from_numpy(qa).cuda(), to_gpu_scales(sa), torch.from_numpy(qb).cuda(),
+                    to_gpu_scales(sb), bs.BS_SCALE_128X128, out=out)
+    torch.cuda.synchronize()
+    check_result(out, qa, sa, qb, sb, 128)
+    check_canaries(full, M, N)
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 384, 640), (384, 256, 1024), (128, 128, 128), (200, 512, 256)])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_scaled_mm_1x128(M, N, K, out_dtype):
+    need_gpu()
+    qa, sa = operand_1x128(M, K, 0.01, seed=M + 5 * K)
+    qb, sb = operand_1x128(N, K, 1.0, seed=N + 7 * K)
+    full, out = guarded(M, N, out_dtype)
+    print(f"scaled_mm 1x128 M={M} N={N} K={K} {out_dtype}", flush=True)
+    bs.bs_scaled_mm(torch.from_numpy(qa).cuda(), to_gpu_scales(sa), torch.from_numpy(qb).cuda(),
+                    to_gpu_scales(sb), bs.BS_SCALE_1X128, out=out)
+    torch.cuda.synchronize()
+    check_result(out, qa, sa, qb, sb, 1)
+    check_canaries(full, M, N)
+
+
+SMALL_INT_CODES = np.array([0xC4, 0xC0, 0xB8, 0x00, 0x38, 0x40, 0x44], dtype=np.uint8)  # -3..3
+
+
+@pytest.mark.parametrize("kind", [bs.BS_SCALE_128X128, bs.BS_SCALE_1X128])
+def test_scaled_mm_exact_small_integers(kind):
+    """Integer codes |v| <= 3 and scales 2^[-2, 2]: every partial sum is exact in
+    fp32, so the fp32 result must equal the float64 oracle bit for bit."""
+    need_gpu()
+    rng = np.random.default_rng(3)
+    M, N, K = 384, 256, 4096
+    qa = rng.choice(SMALL_INT_CODES, size=(M, K))
+    qb = rng.choice(SMALL_INT_CODES, size=(N, K))
+    sa = np.exp2(rng.integers(-2, 3, size=(M, K // 128))).astype(np.float32)
+    rb = 128 if kind == bs.BS_SCALE_128X128 else 1
+    sb = np.exp2(rng.integers(-2, 3, size=(N // rb, K // 128))).astype(np.float32)
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    bs.bs_scaled_mm(torch.from_numpy(qa).cuda(), to_gpu_scales(sa), torch.from_numpy(qb).cuda(),
+                    to_gpu_scales(sb), kind, out=out)
+    torch.cuda.synchronize()
+    check_result(out, qa, sa, qb, sb, rb, exact=True)
+
+
+def test_scaled_mm_identity_b():
+    need_gpu()
+    M, K = 256, 512
+    qa, sa = operand_1x128(M, K, 1.0, seed=11)
+    qb = np.zeros((K, K), dtype=np.uint8)
+    qb[np.arange(K), np.arange(K)] = 0x38
+    sb = np.ones((K // 128, K // 128), dtype=np.float32)
+    out = torch.empty((M, K), dtype=torch.float32, device="cuda")
+    bs.bs_scaled_mm(torch.from_numpy(qa).cuda(), to_gpu_scales(sa), torch.from_numpy(qb).cuda(),
+                    to_gpu_scales(sb), bs.BS_SCALE_128X128, out=out)
+    torch.cuda.synchronize()
+    a = gemm.dequant(qa, sa, 1)
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), a.astype(np.float32).astype(np.float64))
+
+
+def test_scaled_mm_empty_k_writes_zeros():
+    need_gpu()
+    M, N = 256, 256
+    a = torch.empty((M, 16), dtype=torch.uint8, device="cuda")[:, :0]
+    b = torch.empty((N, 16), dtype=torch.uint8, device="cuda")[:, :0]
+    sa = torch.empty((1, 256), dtype=torch.float32, device="cuda")[:0]  # non-NULL, zero rows
+    sb = torch.empty((1, 4), dtype=torch.float32, device="cuda")[:0]
+    out = torch.full((M, N), 7.0, dtype=torch.float32, device="cuda")
+    bs.bs_scaled_mm(a, sa, b, sb, bs.BS_SCALE_128X128, out=out)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
+
+
+def test_b_kinds_agree_on_expanded_scales():
+    need_gpu()
+    M, N, K = 256, 256, 384
+    qa, sa = operand_1x128(M, K, 1.0, seed=21)
+    qb, sb128 = operand_128x128(N, K, 0.02, seed=22)
+    sb1 = np.repeat(sb128, 128, axis=0)
+    ga, gsa, gb = torch.from_numpy(qa).cuda(), to_gpu_scales(sa), torch.from_numpy(qb).cuda()
+    d1 = bs.bs_scaled_mm(ga, gsa, gb, to_gpu_scales(sb128), bs.BS_SCALE_128X128, out_dtype=torch.float32)
+    d2 = bs.bs_scaled_mm(ga, gsa, gb, to_gpu_scales(sb1), bs.BS_SCALE_1X128, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(d1, d2)
+
+
+# ----------------------------------------------------------------------------
+# grouped
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("sizes", [(128, 0, 256), (256, 384, 128, 0), (0, 0, 512), (200, 56, 300)])
+def test_group_m(sizes):
+    need_gpu()
+    G, N, K = len(sizes), 384, 640
+    ends = np.cumsum(sizes).astype(np.int32)
+    M = int(ends[-1])
+    qa, sa = operand_1x128(M, K, 1.0, seed=M + G)
+    w = inputs.bf16_normal((G * N, K), 0.02, seed=G + 100)
+    qw, sw = quant.quant_128x128(bits16(w))  # W as one [G*N, K] matrix
+    # scales K-major [K/128][ld >= G*N/128]; expert g's view starts at column g*N/128
+    sw_gpu = to_gpu_scales(sw)
+    sb_view = torch.as_strided(sw_gpu, (G, K // 128, N // 128), (N // 128, sw_gpu.stride(0), 1))
+    qb = torch.from_numpy(qw).cuda().view(G, N, K)
+    full, out = guarded(M, N, torch.bfloat16)
+    print(f"group_m sizes={sizes}", flush=True)
+    bs.bs_grouped_scaled_mm(bs.BS_GROUP_M, torch.from_numpy(ends).cuda(), torch.from_numpy(qa).cuda(),
+                            to_gpu_scales(sa), qb, sb_view, bs.BS_SCALE_128X128, out=out)
+    torch.cuda.synchronize()
+    d = out.float().cpu().numpy().astype(np.float64)
+    aligned = all(sz % 128 == 0 for sz in sizes)
+    ref = gemm.grouped_mm_group_m(list(ends), qa, sa, qw.reshape(G, N, K),
+                                  sw.reshape(G, N // 128, K // 128), 128) if aligned else None
+    start = 0
+    for g, e in enumerate(ends):
+        if e > start:
+            a = gemm.dequant(qa[start:e], sa[start:e], 1)
+            b = gemm.dequant(qw[g * N:(g + 1) * N], sw[g * N // 128:(g + 1) * N // 128], 128)
+            want = a @ b.T if ref is None else ref[start:e]
+            ok, worst = gemm.check_close(d[start:e], want, a, b)
+            assert ok, f"group {g}: worst {worst}"
+        start = e
+    check_canaries(full, M, N)
+
+
+@pytest.mark.parametrize("sizes", [(256, 0, 128), (128, 128, 128, 128), (0, 384)])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_group_k(sizes, out_dtype):
+    need_gpu()
+    G, M, N = len(sizes), 256, 384
+    ends = np.cumsum(sizes).astype(np.int32)
+    T = int(ends[-1])
+    qa, sa = operand_1x128(M, T, 0.01, seed=T + 1)   # grad_out^T [M, T]
+    qb, sb = operand_1x128(N, T, 1.0, seed=T + 2)    # A^T [N, T]
+    out_full = torch.full((G + 1, M, N), 5.0, dtype=out_dtype, device="cuda")
+    out = out_full[:G]
+    print(f"group_k sizes={sizes} {out_dtype}", flush=True)
+    bs.bs_grouped_scaled_mm(bs.BS_GROUP_K, torch.from_numpy(ends).cuda(), torch.from_numpy(qa).cuda(),
+                            to_gpu_scales(sa), torch.from_numpy(qb).cuda(), to_gpu_scales(sb),
+                            bs.BS_SCALE_1X128, out=out)
+    torch.cuda.synchronize()
+    ref = gemm.grouped_mm_group_k(list(ends), qa, sa, qb, sb)
+    d = out.float().cpu().numpy().astype(np.float64)
+    start = 0
+    for g, e in enumerate(ends):
+        if e == start:
+            assert np.all(d[g] == 0), f"empty group {g} must be zeros"
+        else:
+            a = gemm.dequant(qa[:, start:e], sa[:, start // 128:e // 128], 1)
+            b = gemm.dequant(qb[:, start:e], sb[:, start // 128:e // 128], 1)
+            ok, worst = gemm.check_close(d[g], ref[g], a, b)
+            assert ok, f"group {g}: worst {worst}"
+        start = e
+    assert torch.all(out_full[G] == 5.0)
