@@ -43,6 +43,49 @@ def r4(n):
     return (n + 3) // 4 * 4
 
 
+# bench kernel name -> device kernel symbol (as rocprofv3 names it)
+KERNEL_SYMBOL = {
+    "quant_1x128_rowcol(A)": "quant_1x128_kernel<true, true>",
+    "quant_1x128_rowcol(grad_out)": "quant_1x128_kernel<true, true>",
+    "quant_128x128(W)": "quant_128x128_kernel<false>",
+    "quant_3d_colwise(W)": "quant_128x128_kernel<true>",
+    "gemm_fwd": "gemm_kernel<0, false, false>",
+    "gemm_dgrad": "gemm_kernel<0, false, false>",
+    "gemm_wgrad": "gemm_kernel<0, true, false>",
+    "grouped_gemm_fwd": "gemm_kernel<1, false, false>",
+    "grouped_gemm_dgrad": "gemm_kernel<1, false, false>",
+    "grouped_gemm_wgrad": "gemm_kernel<2, true, false>",
+}
+
+
+def kernel_source_hash():
+    import hashlib
+    src = os.path.join(ROOT, "blockwise_scaled_fp8_bs_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(src)):
+        h.update(open(os.path.join(src, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload, kernel):
+    """HBM-side bytes per launch of `kernel` from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by its reading of a
+    known-size copy), or None when there is none or the kernel sources have
+    changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_rocprof.txt")
+    if not os.path.exists(path):
+        return None
+    sym = KERNEL_SYMBOL.get(kernel)
+    cur = kernel_source_hash()
+    for line in open(path):
+        if line.startswith("traffic_bytes ") and sym and sym in line:
+            fields = line.split()
+            src = fields[-1].split("=", 1)[1]
+            if src == cur:
+                return int(fields[-2])
+    return None
+
+
 class Step:
     """Buffers and launches of one training step of one workload."""
 
@@ -173,7 +216,10 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(inputs.WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before the workload, run a plain device copy of this many MiB three times "
+                         "(a known-size reference for hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -189,6 +235,14 @@ def main():
         print("the forward-only workload is a parity case, not a bench line", file=sys.stderr)
         sys.exit(2)
     torch.manual_seed(args.seed)
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     step = Step(w, seed=args.seed)
     ks = step.kernels()
     stream = torch.cuda.current_stream()
@@ -236,7 +290,7 @@ def main():
         "peak": FP8_PEAK_TFLOPS if d["unit"] == "TFLOP/s" else HBM_PEAK_GBS,
         "unit": d["unit"],
         "frac": d["frac"],
-        "traffic": None,
+        "traffic": counter_traffic(w.name, dom),
     }
     for v in per_kernel.values():
         v.pop("work")
