@@ -178,8 +178,8 @@ bs_status check_gemm_common(const char* fn, int64_t M, int64_t N, int64_t K, con
     REQUIRE(ld_sa % 4 == 0, BS_ERR_LAYOUT, "ld_sa=%lld must be a multiple of 4", (long long)ld_sa);
     REQUIRE(ld_sb % 4 == 0, BS_ERR_LAYOUT, "ld_sb=%lld must be a multiple of 4", (long long)ld_sb);
     // Operand tiles and scale rows are addressed with 32-bit buffer offsets.
-    REQUIRE(lda < (1ll << 23) && ldb < (1ll << 23), BS_ERR_LAYOUT,
-            "lda and ldb must be < 2^23 elements (32-bit tile offsets)");
+    REQUIRE(lda < (1ll << 22) && ldb < (1ll << 22), BS_ERR_LAYOUT,
+            "lda and ldb must be < 2^22 elements (32-bit tile offsets)");
     REQUIRE((K / 128 + 1) * (ld_sa > ld_sb ? ld_sa : ld_sb) < (1ll << 29), BS_ERR_LAYOUT,
             "scale tensors must be smaller than 2 GiB (32-bit offsets)");
     REQUIRE(aligned16(a) && lda % 16 == 0, BS_ERR_ALIGN, "a must be 16-byte aligned with lda %% 16 == 0");

@@ -141,17 +141,45 @@ __device__ __forceinline__ bool resolve_tile(const GemmArgs& p, Tile& t) {
     }
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ lds_void* to_lds(void* p) {
-    return (lds_void*)(__attribute__((address_space(3))) char*)p;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-    // Raw buffer: offsets at or beyond `bytes` read as zero.
+// Raw buffer resource (gfx9 layout): offsets at or beyond `bytes` read as zero.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
     const int32_t n = bytes > 0x7fffffff ? 0x7fffffff : (bytes < 0 ? 0 : (int32_t)bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+    return i32x4{(int32_t)(uint32_t)a, (int32_t)((a >> 32) & 0xffffu), n, 0x00020000};
 }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(size_t)(__attribute__((address_space(3))) const char*)p;
+}
+
+// Global -> LDS copies (buffer_load ... lds): lane i's bytes land at
+// lds_base + i * size.  Issued through inline asm so that the compiler does
+// not wait for them before every LDS read of the other stage (it cannot tell
+// the two stages apart); the kernel waits for them explicitly (vmcnt(0))
+// before the barrier that publishes the stage.
+// Byte address = buffer base + voffset (per lane) + soffset (uniform).
+__device__ __forceinline__ void dma16(i32x4 rs, uint32_t lds_base, int voffset, int soffset) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voffset), "s"(rs),
+                    "s"(__builtin_amdgcn_readfirstlane(soffset)) : "memory");
+}
+
+__device__ __forceinline__ void dma4(i32x4 rs, uint32_t lds_base, int voffset, int soffset) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voffset), "s"(rs),
+                    "s"(__builtin_amdgcn_readfirstlane(soffset)) : "memory");
+}
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 16-byte-chunk swizzle of a 128-byte LDS row: physical chunk = logical ^ swz(row).
+// The 8 lanes of each 128-byte group of an MFMA operand read sit on 8
+// consecutive rows at one logical chunk and land on 8 distinct chunks.
+// (On gfx950's 64-bank LDS, (row ^ row >> 3) & 7 also removes the remaining
+// two-way conflicts between 16-lane groups, but measured no faster here.)
+__device__ __forceinline__ int swz(int row) { return row & 7; }
 
 template <int KIND, bool B1X128, bool OUT_F32>
 __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
@@ -170,46 +198,46 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
     const int64_t rows_a = (tile.m_end - tile.m0) < BM ? (tile.m_end - tile.m0) : BM;
     const int64_t rows_b = (p.N - tile.n0) < BN ? (p.N - tile.n0) : BN;
     const int64_t nkb_all = p.K / BK;
-    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(p.a + tile.m0 * p.lda, rows_a * p.lda);
-    const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(tile.b + tile.n0 * p.ldb, rows_b * p.ldb);
-    const __amdgpu_buffer_rsrc_t rs_sa =
-        make_rsrc(p.sa + tile.m0, ((nkb_all - 1) * p.ld_sa + (p.M - tile.m0)) * 4);
+    const i32x4 rs_a = make_rsrc(p.a + tile.m0 * p.lda, rows_a * p.lda);
+    const i32x4 rs_b = make_rsrc(tile.b + tile.n0 * p.ldb, rows_b * p.ldb);
+    const i32x4 rs_sa = make_rsrc(p.sa + tile.m0, ((nkb_all - 1) * p.ld_sa + (p.M - tile.m0)) * 4);
     const int64_t nb_count = (p.N + BK - 1) / BK;
-    const __amdgpu_buffer_rsrc_t rs_sb =
+    const i32x4 rs_sb =
         B1X128 ? make_rsrc(tile.sb + tile.n0, ((nkb_all - 1) * p.ld_sb + (p.N - tile.n0)) * 4)
                : make_rsrc(tile.sb, ((nkb_all - 1) * p.ld_sb + nb_count) * 4);
 
     // Wave w fills LDS rows [(8i + w) * 8, +8) of each operand in round i
     // (1 KiB: lane l -> physical chunk l % 8 of row l / 8, which holds the
-    // logical chunk (l % 8) ^ (l / 8) under the row-XOR swizzle).
+    // logical chunk (l % 8) ^ swz(row); swz sees bits 0..3 of the row, i.e.
+    // l / 8 and the parity of w).
     const int ld_lrow = lane >> 3;
-    const int ld_lchunk = (lane & 7) ^ ld_lrow;
+    const int ld_lchunk = (lane & 7) ^ swz(w * 8 + ld_lrow);
     const int sb_nb = (int)(tile.n0 / BK);
 
+    // Loop-invariant lane offsets; the K block and the round's 64-row step
+    // enter through the uniform soffset.
+    const int voff_a = (int)((w * 8 + ld_lrow) * p.lda) + ld_lchunk * 16;
+    const int voff_b = (int)((w * 8 + ld_lrow) * p.ldb) + ld_lchunk * 16;
+    const int voff_s = B1X128 ? lane * 16 : (sb_nb + lane) * 4;
+
     auto issue_loads = [&](int64_t kb, int s) {
+        const int k_off = (int)(kb * BK);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = (8 * i + w) * 8 + ld_lrow;
-            const int off_a = (int)(row * p.lda + kb * BK) + ld_lchunk * 16;
-            const int off_b = (int)(row * p.ldb + kb * BK) + ld_lchunk * 16;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, to_lds(&sm.a[s][(8 * i + w) * 1024]), 16, off_a, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, to_lds(&sm.b[s][(8 * i + w) * 1024]), 16, off_b, 0, 0, 0);
+            dma16(rs_a, lds_addr(&sm.a[s][(8 * i + w) * 1024]), voff_a, k_off + (int)(64 * i * p.lda));
+            dma16(rs_b, lds_addr(&sm.b[s][(8 * i + w) * 1024]), voff_b, k_off + (int)(64 * i * p.ldb));
         }
         if (w == 0) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_sa, to_lds(&sm.sa[s][0]), 16,
-                                                     (int)(kb * p.ld_sa * 4) + lane * 16, 0, 0, 0);
+            dma16(rs_sa, lds_addr(&sm.sa[s][0]), lane * 16, (int)(kb * p.ld_sa * 4));
         } else if (w == 1) {
-            if (B1X128) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_sb, to_lds(&sm.sb[s][0]), 16,
-                                                         (int)(kb * p.ld_sb * 4) + lane * 16, 0, 0, 0);
-            } else if (lane < 2) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_sb, to_lds(&sm.sb[s][0]), 4,
-                                                         (int)((kb * p.ld_sb + sb_nb) * 4) + lane * 4, 0, 0, 0);
-            }
+            if (B1X128)
+                dma16(rs_sb, lds_addr(&sm.sb[s][0]), voff_s, (int)(kb * p.ld_sb * 4));
+            else if (lane < 2)
+                dma4(rs_sb, lds_addr(&sm.sb[s][0]), voff_s, (int)(kb * p.ld_sb * 4));
         }
     };
     auto frag = [&](const uint8_t* base, int row) -> v8i {
-        const int sw = row & 7;
+        const int sw = swz(row);
         const uint4 lo = *reinterpret_cast<const uint4*>(base + row * BK + (((2 * lg) ^ sw) * 16));
         const uint4 hi = *reinterpret_cast<const uint4*>(base + row * BK + (((2 * lg + 1) ^ sw) * 16));
         v8i r;
@@ -218,6 +246,9 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
         return r;
     };
 
+    // The MFMA computes the transposed tile (B rows as its first operand), so
+    // lane l holds, for MFMA tile (i, j), row  wm*WM + 16i + (l % 16)  and the
+    // four consecutive columns  wn*WN + 16j + 4(l / 16) + r,  r = 0..3.
     v4f acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -226,57 +257,86 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
 
     const int64_t nkb = tile.kb1 > tile.kb0 ? tile.kb1 - tile.kb0 : 0;
     if (nkb > 0) issue_loads(tile.kb0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_dma();
     __syncthreads();
 
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t it = 0; it < nkb; ++it) {
-        const int s = (int)(it & 1);
+    // One K block on LDS stage s (a compile-time constant at both call sites).
+    auto step = [&](int64_t it, const int s) {
         if (it + 1 < nkb) issue_loads(tile.kb0 + it + 1, s ^ 1);
-
+        // Operand reads in the order the MFMAs consume them, so that the
+        // first MFMA waits for two fragments only (every wave reads right
+        // after the barrier); the scales are needed later, by the fmas.
+        v8i af_next = frag(sm.a[s], wm * WM + lr);
         v8i bf[TN];
-        float sbj[TN];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int nrow = wn * WN + j * 16 + lr;
-            bf[j] = frag(sm.b[s], nrow);
-            sbj[j] = B1X128 ? sm.sb[s][nrow] : sm.sb[s][wn >> 1];
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const v8i af = frag(sm.a[s], wm * WM + i * 16 + lr);
-            const float4 sa4 = *reinterpret_cast<const float4*>(&sm.sa[s][wm * WM + i * 16 + 4 * lg]);
+        for (int j = 0; j < TN; ++j) bf[j] = frag(sm.b[s], wn * WN + j * 16 + lr);
+        v4f sbv[TN];  // B scale of each of the lane's output columns
+        if (B1X128) {
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                const v4f pk = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], zero, 0, 0, 0, 0,
-                                                                                  0, 0);
-                acc[i][j][0] = __builtin_fmaf(pk[0], sa4.x * sbj[j], acc[i][j][0]);
-                acc[i][j][1] = __builtin_fmaf(pk[1], sa4.y * sbj[j], acc[i][j][1]);
-                acc[i][j][2] = __builtin_fmaf(pk[2], sa4.z * sbj[j], acc[i][j][2]);
-                acc[i][j][3] = __builtin_fmaf(pk[3], sa4.w * sbj[j], acc[i][j][3]);
+                const float4 t4 = *reinterpret_cast<const float4*>(&sm.sb[s][wn * WN + j * 16 + 4 * lg]);
+                sbv[j] = v4f{t4.x, t4.y, t4.z, t4.w};
             }
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    }
+        const float sbw = B1X128 ? 0.f : sm.sb[s][wn >> 1];
+        float sa_i[TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) sa_i[i] = sm.sa[s][wm * WM + i * 16 + lr];
 
-    // ---- epilogue: D[m, n] for m < m_end, n < N ----
+        // Software pipeline at MFMA granularity: the scale fmas of tile
+        // (i, j) run while the MFMA of the next tile executes.
+        v4f pbuf[2];
+        int pi = 0, pj = 0;
+        auto fold = [&](const v4f& pk, int i, int j) {
+            if (B1X128) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[i][j][r] = __builtin_fmaf(pk[r], sa_i[i] * sbv[j][r], acc[i][j][r]);
+            } else {
+                const float sc = sa_i[i] * sbw;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pk[r], sc, acc[i][j][r]);
+            }
+        };
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const v8i af = af_next;
+            if (i + 1 < TM) af_next = frag(sm.a[s], wm * WM + (i + 1) * 16 + lr);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int t = i * TN + j;
+                pbuf[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, zero, 0, 0, 0, 0, 0, 0);
+                if (t > 0) fold(pbuf[(t - 1) & 1], pi, pj);
+                pi = i;
+                pj = j;
+            }
+        }
+        fold(pbuf[(TM * TN - 1) & 1], TM - 1, TN - 1);
+        wait_dma();
+        __syncthreads();
+    };
+    for (int64_t it = 0; it < nkb; ++it) step(it, (int)(it & 1));
+
+    // ---- epilogue: four consecutive columns per lane and tile ----
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
+        const int64_t m = tile.m0 + wm * WM + i * 16 + lr;
+        if (m >= tile.m_end) continue;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int64_t n = tile.n0 + wn * WN + j * 16 + lr;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t m = tile.m0 + wm * WM + i * 16 + 4 * lg + r;
-                if (m < tile.m_end && n < p.N) {
-                    if (OUT_F32) {
-                        reinterpret_cast<float*>(dbase)[m * p.ldd + n] = acc[i][j][r];
-                    } else {
-                        const __bf16 h = (__bf16)acc[i][j][r];
-                        reinterpret_cast<uint16_t*>(dbase)[m * p.ldd + n] = __builtin_bit_cast(uint16_t, h);
-                    }
-                }
+            const int64_t n = tile.n0 + wn * WN + j * 16 + 4 * lg;
+            if (n >= p.N) continue;
+            const v4f v = acc[i][j];
+            if (OUT_F32) {
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(dbase) + m * p.ldd + n) =
+                    make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+                const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[0]) |
+                                    ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[1]) << 16);
+                const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2]) |
+                                    ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(dbase) + m * p.ldd + n) = make_uint2(lo, hi);
             }
         }
     }
