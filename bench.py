@@ -295,6 +295,22 @@ def main():
     for v in per_kernel.values():
         v.pop("work")
 
+    # Practical HBM reference: a plain device copy of 1 GiB (torch copy_),
+    # timed the same way.  The fractions above use the published 8 TB/s peak.
+    n_copy = 1 << 30
+    src = torch.empty(n_copy, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n_copy * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+
     cpu = None
     if not args.no_cpu_baseline:
         tflops, secs, desc = cpu_oracle_sample(w, rows=args.cpu_rows, seed=args.seed)
@@ -320,6 +336,8 @@ def main():
         "gemm_frac_of_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
         "quant_gbs": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
         "quant_frac_of_hbm": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "hbm_copy_gbs": round(copy_gbs, 1),
+        "quant_frac_of_copy": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / copy_gbs, 4),
         "kernels": per_kernel,
         "roofline": roofline,
         "cpu_baseline": cpu,

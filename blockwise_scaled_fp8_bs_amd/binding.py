@@ -241,7 +241,7 @@ def bs_grouped_scaled_mm(mode, group_end, a, sa, b, sb, b_kind, out=None, out_dt
 # ----------------------------------------------------------------------------
 
 def bs_diag_e4m3_census(device="cuda", stream=None):
-    """(min_bits, max_bits, counts) per e4m3 code over all |y| <= 448 (CPU tensors)."""
+    """(min_bits, max_bits, counts) per e4m3 code over all |y| <= 464 (CPU tensors)."""
     mn = torch.empty(256, dtype=torch.int32, device=device)
     mx = torch.empty(256, dtype=torch.int32, device=device)
     cnt = torch.empty(256, dtype=torch.int64, device=device)

@@ -6,9 +6,9 @@ namespace bs {
 
 namespace {
 
-constexpr uint32_t kBits448 = 0x43E00000u;  // 448.0f
+constexpr uint32_t kBits464 = 0x43E80000u;  // 464.0f
 
-// Census of the encode step over all |y| <= 448, both signs.
+// Census of the hot-path encode step (no clamp) over all |y| <= 464, both signs.
 __global__ __launch_bounds__(256) void census_kernel(uint32_t* min_bits, uint32_t* max_bits,
                                                      unsigned long long* counts) {
     __shared__ uint32_t s_min[256], s_max[256];
@@ -19,7 +19,7 @@ __global__ __launch_bounds__(256) void census_kernel(uint32_t* min_bits, uint32_
         s_cnt[i] = 0ull;
     }
     __syncthreads();
-    const uint64_t total = (uint64_t)kBits448 + 1;  // magnitudes 0 .. 448 inclusive
+    const uint64_t total = (uint64_t)kBits464 + 1;  // magnitudes 0 .. 464 inclusive
     const uint64_t per = (total + gridDim.x - 1) / gridDim.x;
     const uint64_t b0 = (uint64_t)blockIdx.x * per;
     const uint64_t b1 = b0 + per < total ? b0 + per : total;
@@ -70,7 +70,9 @@ __global__ void census_init(uint32_t* min_bits, uint32_t* max_bits, unsigned lon
 // One workgroup per amax candidate: every positive finite bf16 (bits
 // 0x0001 .. 0x7F7F) plus amax = 0, which takes the EPS floor.  Every finite
 // bf16 x with |x| <= max(amax, EPS) is divided by the block scale with the
-// quantizers' routine and with the IEEE division.
+// quantizers' routine and with the IEEE division; the codes of the
+// routine (encode4, no clamp) are compared with the definition's codes
+// (IEEE quotient, clamp, round).
 // result[0] pairs checked, [1] scale mismatches, [2] e4m3 code mismatches,
 // [3] quotient mismatches with |x/s| >= 2^-10, [4] quotient mismatches with
 // |x/s| < 2^-10 (these encode to a signed zero either way; informational).
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(256) void division_kernel(unsigned long long* resul
             const float y = div_by_scale(x, sc);
             const float y_ieee = x / s_ieee;
             ++c[0];
-            if ((encode4(y, 0.f, 0.f, 0.f) & 0xffu) != (encode4(y_ieee, 0.f, 0.f, 0.f) & 0xffu)) ++c[2];
+            if ((encode4(y, 0.f, 0.f, 0.f) & 0xffu) != encode_clamped(y_ieee)) ++c[2];
             if (__float_as_uint(y) != __float_as_uint(y_ieee)) {
                 if (fabsf(y_ieee) >= 0.0009765625f) ++c[3];
                 else ++c[4];

@@ -13,7 +13,12 @@
 //    tile so that the global stores are full 128-byte rows of q^T.
 //  * 128x128 blocks: one amax per tile (thread -> DPP row -> wave -> LDS).
 //
-// Each tile reads HBM once and writes each requested output once.
+// Workgroups are persistent: each walks the tiles with a grid stride and
+// loads the next tile's bf16 data into registers before working on the
+// current one, so HBM reads overlap the arithmetic and no partly filled last
+// wave of workgroups is left.  LDS buffers alternate between consecutive
+// tiles, so one barrier per LDS exchange suffices.  Each tile reads HBM once
+// and writes each requested output once.
 #include "bs_kernels.h"
 #include "bs_device.h"
 
@@ -24,29 +29,52 @@ namespace {
 constexpr int kTile = 128;
 constexpr int kThreads = 256;
 
+struct Raw {
+    uint4 v[8];  // v[i]: row 8*tr + i, columns 8*tc .. +7 (bf16)
+};
+
 struct TileRegs {
     float f[8][8];  // f[i][j]: row 8*tr + i, column 8*tc + j of the tile
 };
 
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int64_t ld_x, int64_t r0,
-                                          int64_t c0, int64_t R, int tr, int tc, TileRegs& t) {
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Raw buffer over [base, base + bytes): loads past the end read zero and
+// stores past the end are dropped, which handles ragged tiles without
+// per-lane bounds checks; the tile origin lives in the (scalar) descriptor
+// and lanes keep 32-bit offsets.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+    const int32_t n = bytes > 0x7fffffff ? 0x7fffffff : (bytes < 0 ? 0 : (int32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// Rows [r0, r0 + 128) of a tile whose first column is c0; rows >= R read as 0.
+__device__ __forceinline__ void load_raw(const uint16_t* __restrict__ x, int64_t ld_x, int64_t r0, int64_t c0,
+                                         int64_t R, int voff, Raw& raw) {
+    const int64_t rows = (R - r0) < kTile ? (R - r0) : kTile;
+    const __amdgpu_buffer_rsrc_t rx = rsrc(x + r0 * ld_x + c0, rows * ld_x * 2);
+    const int row_bytes = (int)(ld_x * 2);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int64_t row = r0 + 8 * tr + i;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (row < R) v = *reinterpret_cast<const uint4*>(x + row * ld_x + c0 + 8 * tc);
-        unpack8(v, t.f[i]);
+        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff, i * row_bytes, 0));
+        raw.v[i] = make_uint4(v[0], v[1], v[2], v[3]);
     }
+}
+
+__device__ __forceinline__ void unpack_tile(const Raw& raw, TileRegs& t) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) unpack8(raw.v[i], t.f[i]);
 }
 
 // Transposed store of an 8x8 block of codes per thread through LDS.
 // codes[j] holds the 8 codes of column 8*tc + j for rows 8*tr .. 8*tr + 7.
 // LDS tile: row c (a column of the source) is 128 bytes = 16 chunks of 8
 // bytes; chunk tr is stored at physical chunk tr ^ tc, which spreads the 16
-// lanes of a DPP row over all banks.
+// lanes of a DPP row over all banks.  `out` points at output row 0, column 0
+// of the tile; 8 lanes write each 128-byte output row.
 __device__ __forceinline__ void store_transposed(uint8_t* lds, const uint2* codes, int tr, int tc,
-                                                 uint8_t* __restrict__ out, int64_t ld_out,
-                                                 int64_t out_row0, int64_t out_col0) {
+                                                 uint8_t* __restrict__ out, int64_t ld_out) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int c = 8 * tc + j;
@@ -54,6 +82,8 @@ __device__ __forceinline__ void store_transposed(uint8_t* lds, const uint2* code
     }
     __syncthreads();
     const int t = threadIdx.x;
+    const __amdgpu_buffer_rsrc_t ro = rsrc(out, (kTile - 1) * ld_out + kTile);
+    const int voff = (t >> 3) * (int)ld_out + 16 * (t & 7);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int c = p * 32 + (t >> 3);
@@ -64,167 +94,218 @@ __device__ __forceinline__ void store_transposed(uint8_t* lds, const uint2* code
         if (sw & 1) {  // the pair is stored swapped
             v = make_uint4(v.z, v.w, v.x, v.y);
         }
-        *reinterpret_cast<uint4*>(out + (out_row0 + c) * ld_out + out_col0 + 16 * k) = v;
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, ro, voff, p * 32 * (int)ld_out, 0);
+    }
+}
+
+__device__ __forceinline__ void col_codes(const TileRegs& tile, const Scale* sc, uint2* codes) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        codes[j].x = encode4(div_by_scale(tile.f[0][j], sc[j]), div_by_scale(tile.f[1][j], sc[j]),
+                             div_by_scale(tile.f[2][j], sc[j]), div_by_scale(tile.f[3][j], sc[j]));
+        codes[j].y = encode4(div_by_scale(tile.f[4][j], sc[j]), div_by_scale(tile.f[5][j], sc[j]),
+                             div_by_scale(tile.f[6][j], sc[j]), div_by_scale(tile.f[7][j], sc[j]));
     }
 }
 
 template <bool ROW, bool COL>
 __global__ __launch_bounds__(kThreads) void quant_1x128_kernel(Quant1x128Args a) {
-    __shared__ float s_colmax[4][kTile];
-    __shared__ __attribute__((aligned(16))) uint8_t s_tr[COL ? kTile * kTile : 16];
+    __shared__ float s_colmax[2][4][kTile];
+    __shared__ __attribute__((aligned(16))) uint8_t s_tr[COL ? 2 : 1][COL ? kTile * kTile : 16];
 
     const int t = threadIdx.x;
     const int tr = t >> 4, tc = t & 15;
     const int wave = t >> 6;
-    const int64_t ct = blockIdx.x % a.col_tiles;
-    const int64_t rt = blockIdx.x / a.col_tiles;
-    const int64_t r0 = rt * kTile, c0 = ct * kTile;
+    const int64_t ntiles = ((a.R + kTile - 1) / kTile) * a.col_tiles;
 
-    TileRegs tile;
-    load_tile(a.x, a.ld_x, r0, c0, a.R, tr, tc, tile);
+    int64_t tile = blockIdx.x;
+    if (tile >= ntiles) return;
+    const int voff_x = (8 * tr) * (int)(a.ld_x * 2) + 16 * tc;
+    Raw raw;
+    load_raw(a.x, a.ld_x, (tile / a.col_tiles) * kTile, (tile % a.col_tiles) * kTile, a.R, voff_x, raw);
 
-    if (ROW) {
-        float my_scale = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float m = 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(tile.f[i][j]));
-            const uint32_t amax_bits = row16_max(__float_as_uint(m));
-            const Scale sc = block_scale(__uint_as_float(amax_bits));
-            const int64_t row = r0 + 8 * tr + i;
-            const uint2 q = quant8(tile.f[i], sc);
-            if (row < a.R) *reinterpret_cast<uint2*>(a.q_row + row * a.ld_qr + c0 + 8 * tc) = q;
-            if ((tc & 7) == i) my_scale = sc.s;
-        }
-        // lanes tc < 8 store the scale of row 8*tr + tc: 32 consecutive rows per wave
-        const int64_t row = r0 + 8 * tr + tc;
-        if (tc < 8 && row < a.R) a.s_row[(c0 / kTile) * a.ld_sr + row] = my_scale;
-    }
+    for (int parity = 0; tile < ntiles; tile += gridDim.x, parity ^= 1) {
+        const int64_t r0 = (tile / a.col_tiles) * kTile, c0 = (tile % a.col_tiles) * kTile;
+        TileRegs tl;
+        unpack_tile(raw, tl);
+        const int64_t next = tile + gridDim.x;
+        if (next < ntiles)
+            load_raw(a.x, a.ld_x, (next / a.col_tiles) * kTile, (next % a.col_tiles) * kTile, a.R, voff_x, raw);
 
-    if (COL) {
-        // column amax over the tile's 128 rows
-        float cm[8];
+        if (ROW) {
+            const int64_t rows = (a.R - r0) < kTile ? (a.R - r0) : kTile;
+            const __amdgpu_buffer_rsrc_t rq = rsrc(a.q_row + r0 * a.ld_qr + c0, rows * a.ld_qr);
+            const int voff_q = (8 * tr) * (int)a.ld_qr + 8 * tc;
+            float my_scale = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float m = 0.f;
+            for (int i = 0; i < 8; ++i) {
+                float m = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(tile.f[i][j]));
-            m = fmaxf(m, __shfl_xor(m, 16));
-            m = fmaxf(m, __shfl_xor(m, 32));
-            cm[j] = m;
+                for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(tl.f[i][j]));
+                const uint32_t amax_bits = row16_max(__float_as_uint(m));
+                const Scale sc = block_scale(__uint_as_float(amax_bits));
+                const uint2 q = quant8(tl.f[i], sc);
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{q.x, q.y}, rq, voff_q, i * (int)a.ld_qr, 0);
+                if ((tc & 7) == i) my_scale = sc.s;
+            }
+            // lanes tc < 8 store the scale of row 8*tr + tc: 32 consecutive rows per wave
+            const __amdgpu_buffer_rsrc_t rs = rsrc(a.s_row + (c0 / kTile) * a.ld_sr + r0, rows * 4);
+            if (tc < 8) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(my_scale), rs, (8 * tr + tc) * 4, 0, 0);
         }
-        if ((t & 63) < 16) {
+
+        if (COL) {
+            // column amax over the tile's 128 rows
+            float cm[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) s_colmax[wave][8 * tc + j] = cm[j];
-        }
-        __syncthreads();
-        Scale sc[8];
+            for (int j = 0; j < 8; ++j) {
+                float m = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int c = 8 * tc + j;
-            const float m = fmaxf(fmaxf(s_colmax[0][c], s_colmax[1][c]),
-                                  fmaxf(s_colmax[2][c], s_colmax[3][c]));
-            sc[j] = block_scale(m);
-        }
-        uint2 codes[8];
+                for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(tl.f[i][j]));
+                m = fmaxf(m, __shfl_xor(m, 16));
+                m = fmaxf(m, __shfl_xor(m, 32));
+                cm[j] = m;
+            }
+            if ((t & 63) < 16) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            codes[j].x = encode4(div_by_scale(tile.f[0][j], sc[j]), div_by_scale(tile.f[1][j], sc[j]),
-                                 div_by_scale(tile.f[2][j], sc[j]), div_by_scale(tile.f[3][j], sc[j]));
-            codes[j].y = encode4(div_by_scale(tile.f[4][j], sc[j]), div_by_scale(tile.f[5][j], sc[j]),
-                                 div_by_scale(tile.f[6][j], sc[j]), div_by_scale(tile.f[7][j], sc[j]));
+                for (int j = 0; j < 8; ++j) s_colmax[parity][wave][8 * tc + j] = cm[j];
+            }
+            __syncthreads();
+            Scale sc[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int c = 8 * tc + j;
+                const float m = fmaxf(fmaxf(s_colmax[parity][0][c], s_colmax[parity][1][c]),
+                                      fmaxf(s_colmax[parity][2][c], s_colmax[parity][3][c]));
+                sc[j] = block_scale(m);
+            }
+            uint2 codes[8];
+            col_codes(tl, sc, codes);
+            if (t < 16) {
+                const __amdgpu_buffer_rsrc_t rs = rsrc(a.s_col + (r0 / kTile) * a.ld_sc + c0, kTile * 4);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    u32x4{__float_as_uint(sc[0].s), __float_as_uint(sc[1].s), __float_as_uint(sc[2].s),
+                          __float_as_uint(sc[3].s)}, rs, 32 * tc, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    u32x4{__float_as_uint(sc[4].s), __float_as_uint(sc[5].s), __float_as_uint(sc[6].s),
+                          __float_as_uint(sc[7].s)}, rs, 32 * tc + 16, 0, 0);
+            }
+            store_transposed(s_tr[parity], codes, tr, tc, a.q_col + c0 * a.ld_qc + r0, a.ld_qc);
         }
-        if (t < 16) {
-            float* dst = a.s_col + (r0 / kTile) * a.ld_sc + c0 + 8 * tc;
-            *reinterpret_cast<float4*>(dst) = make_float4(sc[0].s, sc[1].s, sc[2].s, sc[3].s);
-            *reinterpret_cast<float4*>(dst + 4) = make_float4(sc[4].s, sc[5].s, sc[6].s, sc[7].s);
-        }
-        store_transposed(s_tr, codes, tr, tc, a.q_col, a.ld_qc, c0, r0);
     }
 }
 
 // 128x128 quantizer; TRANSPOSE writes the tile transposed (3-D colwise).
 template <bool TRANSPOSE>
 __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(Quant128Args a) {
-    __shared__ float s_wmax[4];
-    __shared__ __attribute__((aligned(16))) uint8_t s_tr[TRANSPOSE ? kTile * kTile : 16];
+    __shared__ float s_wmax[2][4];
+    __shared__ __attribute__((aligned(16))) uint8_t s_tr[TRANSPOSE ? 2 : 1][TRANSPOSE ? kTile * kTile : 16];
 
     const int t = threadIdx.x;
     const int tr = t >> 4, tc = t & 15;
     const int wave = t >> 6;
     const int64_t per_g = a.row_tiles * a.col_tiles;
-    const int64_t g = blockIdx.x / per_g;
-    const int64_t rem = blockIdx.x % per_g;
-    const int64_t rt = rem / a.col_tiles, ct = rem % a.col_tiles;
-    const int64_t r0 = rt * kTile, c0 = ct * kTile;
-    const uint16_t* x = a.x + g * a.stride_xg;
+    const int64_t ntiles = a.G * per_g;
 
-    TileRegs tile;
-    load_tile(x, a.ld_x, r0, c0, a.R, tr, tc, tile);
+    auto coords = [&](int64_t tl_id, int64_t& g, int64_t& rt, int64_t& ct) {
+        g = tl_id / per_g;
+        const int64_t rem = tl_id % per_g;
+        rt = rem / a.col_tiles;
+        ct = rem % a.col_tiles;
+    };
 
-    float m = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(tile.f[i][j]));
-    uint32_t mb = row16_max(__float_as_uint(m));
-    mb = max(mb, (uint32_t)__shfl_xor((int)mb, 16));
-    mb = max(mb, (uint32_t)__shfl_xor((int)mb, 32));
-    if ((t & 63) == 0) s_wmax[wave] = __uint_as_float(mb);
-    __syncthreads();
-    const float amax = fmaxf(fmaxf(s_wmax[0], s_wmax[1]), fmaxf(s_wmax[2], s_wmax[3]));
-    const Scale sc = block_scale(amax);
+    int64_t tile = blockIdx.x;
+    if (tile >= ntiles) return;
+    const int voff_x = (8 * tr) * (int)(a.ld_x * 2) + 16 * tc;
+    int64_t g, rt, ct;
+    coords(tile, g, rt, ct);
+    Raw raw;
+    load_raw(a.x + g * a.stride_xg, a.ld_x, rt * kTile, ct * kTile, a.R, voff_x, raw);
 
-    uint8_t* q = a.q + g * a.stride_qg;
-    if (!TRANSPOSE) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int64_t row = r0 + 8 * tr + i;
-            *reinterpret_cast<uint2*>(q + row * a.ld_q + c0 + 8 * tc) = quant8(tile.f[i], sc);
+    for (int parity = 0; tile < ntiles; tile += gridDim.x, parity ^= 1) {
+        coords(tile, g, rt, ct);
+        const int64_t r0 = rt * kTile, c0 = ct * kTile;
+        TileRegs tl;
+        unpack_tile(raw, tl);
+        const int64_t next = tile + gridDim.x;
+        if (next < ntiles) {
+            int64_t ng, nrt, nct;
+            coords(next, ng, nrt, nct);
+            load_raw(a.x + ng * a.stride_xg, a.ld_x, nrt * kTile, nct * kTile, a.R, voff_x, raw);
         }
-        if (t == 0) a.s[g * a.stride_sg + ct * a.ld_s + rt] = sc.s;
-    } else {
-        uint2 codes[8];
+
+        float m = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            codes[j].x = encode4(div_by_scale(tile.f[0][j], sc), div_by_scale(tile.f[1][j], sc),
-                                 div_by_scale(tile.f[2][j], sc), div_by_scale(tile.f[3][j], sc));
-            codes[j].y = encode4(div_by_scale(tile.f[4][j], sc), div_by_scale(tile.f[5][j], sc),
-                                 div_by_scale(tile.f[6][j], sc), div_by_scale(tile.f[7][j], sc));
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(tl.f[i][j]));
+        uint32_t mb = row16_max(__float_as_uint(m));
+        mb = max(mb, (uint32_t)__shfl_xor((int)mb, 16));
+        mb = max(mb, (uint32_t)__shfl_xor((int)mb, 32));
+        if ((t & 63) == 0) s_wmax[parity][wave] = __uint_as_float(mb);
+        __syncthreads();
+        const float amax = fmaxf(fmaxf(s_wmax[parity][0], s_wmax[parity][1]),
+                                 fmaxf(s_wmax[parity][2], s_wmax[parity][3]));
+        const Scale sc = block_scale(amax);
+
+        uint8_t* q = a.q + g * a.stride_qg;
+        if (!TRANSPOSE) {
+            const __amdgpu_buffer_rsrc_t rq = rsrc(q + r0 * a.ld_q + c0, (kTile - 1) * a.ld_q + kTile);
+            const int voff_q = (8 * tr) * (int)a.ld_q + 8 * tc;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint2 c8 = quant8(tl.f[i], sc);
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{c8.x, c8.y}, rq, voff_q, i * (int)a.ld_q, 0);
+            }
+            if (t == 0) a.s[g * a.stride_sg + ct * a.ld_s + rt] = sc.s;
+        } else {
+            Scale scs[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) scs[j] = sc;
+            uint2 codes[8];
+            col_codes(tl, scs, codes);
+            if (t == 0) a.s[g * a.stride_sg + rt * a.ld_s + ct] = sc.s;
+            store_transposed(s_tr[parity], codes, tr, tc, q + c0 * a.ld_q + r0, a.ld_q);
         }
-        if (t == 0) a.s[g * a.stride_sg + rt * a.ld_s + ct] = sc.s;
-        store_transposed(s_tr, codes, tr, tc, q, a.ld_q, c0, r0);
     }
+}
+
+// Persistent grid: as many workgroups as fit on the device at once (per the
+// kernel's occupancy), never more than the tiles.
+template <typename K>
+int64_t persistent_blocks(K kernel, int64_t tiles) {
+    int dev = 0, cus = 256, per_cu = 2;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, 0) == hipSuccess && occ > 0) per_cu = occ;
+    const int64_t cap = (int64_t)cus * per_cu;
+    return tiles < cap ? tiles : cap;
 }
 
 }  // namespace
 
-hipError_t launch_quant_1x128(const Quant1x128Args& a, bool row, bool col, hipStream_t stream) {
-    const int64_t row_tiles = (a.R + kTile - 1) / kTile;
-    const int64_t blocks = row_tiles * a.col_tiles;
-    if (blocks == 0) return hipSuccess;
-    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    dim3 grid((unsigned)blocks), block(kThreads);
-    if (row && col)
-        hipLaunchKernelGGL((quant_1x128_kernel<true, true>), grid, block, 0, stream, a);
-    else if (row)
-        hipLaunchKernelGGL((quant_1x128_kernel<true, false>), grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL((quant_1x128_kernel<false, true>), grid, block, 0, stream, a);
+template <typename K, typename A>
+hipError_t launch_persistent(K kernel, const A& a, int64_t tiles, hipStream_t stream) {
+    dim3 grid((unsigned)persistent_blocks(kernel, tiles)), block(kThreads);
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
+hipError_t launch_quant_1x128(const Quant1x128Args& a, bool row, bool col, hipStream_t stream) {
+    const int64_t tiles = ((a.R + kTile - 1) / kTile) * a.col_tiles;
+    if (tiles == 0) return hipSuccess;
+    if (row && col) return launch_persistent(quant_1x128_kernel<true, true>, a, tiles, stream);
+    if (row) return launch_persistent(quant_1x128_kernel<true, false>, a, tiles, stream);
+    return launch_persistent(quant_1x128_kernel<false, true>, a, tiles, stream);
+}
+
 hipError_t launch_quant_128x128(const Quant128Args& a, bool transpose, hipStream_t stream) {
-    const int64_t blocks = a.G * a.row_tiles * a.col_tiles;
-    if (blocks == 0) return hipSuccess;
-    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    dim3 grid((unsigned)blocks), block(kThreads);
-    if (transpose)
-        hipLaunchKernelGGL((quant_128x128_kernel<true>), grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL((quant_128x128_kernel<false>), grid, block, 0, stream, a);
-    return hipGetLastError();
+    const int64_t tiles = a.G * a.row_tiles * a.col_tiles;
+    if (tiles == 0) return hipSuccess;
+    if (transpose) return launch_persistent(quant_128x128_kernel<true>, a, tiles, stream);
+    return launch_persistent(quant_128x128_kernel<false>, a, tiles, stream);
 }
 
 }  // namespace bs

@@ -226,13 +226,15 @@ const char* bs_last_error(void);
  * ------------------------------------------------------------------------ */
 
 /*
- * bs_diag_e4m3_census -- applies the quantizers' final step (clamp to
- * [-448, 448], then round to e4m3) to EVERY float32 value y with |y| <= 448
- * of both signs and records, per output code c (0..255), the smallest and
- * largest |y| bit pattern (sign bit cleared) that produced it and how many
- * did.  Outputs: device uint32 min_bits[256], max_bits[256], uint64
- * counts[256]; codes never produced have count 0.  Monotone rounding gives
- * max_bits - min_bits + 1 == count for every produced code.
+ * bs_diag_e4m3_census -- applies the quantizers' encode step (round to e4m3,
+ * nearest even) to EVERY float32 value y with |y| <= 464 of both signs and
+ * records, per output code c (0..255), the smallest and largest |y| bit
+ * pattern (sign bit cleared) that produced it and how many did.  (Quantizer
+ * quotients stay within 448 * (1 + 2^-23); the range up to 464 shows the
+ * step saturates there without a clamp.)  Outputs: device uint32
+ * min_bits[256], max_bits[256], uint64 counts[256]; codes never produced
+ * have count 0.  Monotone rounding gives max_bits - min_bits + 1 == count
+ * for every produced code.
  */
 bs_status bs_diag_e4m3_census(uint32_t* min_bits, uint32_t* max_bits,
                               unsigned long long* counts, hipStream_t stream);
