@@ -216,7 +216,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(inputs.WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--cpu-rows", type=int, default=8192,
+                    help="tokens of the workload the CPU oracle baseline runs on (capped at M)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before the workload, run a plain device copy of this many MiB three times "
                          "(a known-size reference for hardware byte counters)")
@@ -313,7 +314,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        tflops, secs, desc = cpu_oracle_sample(w, rows=args.cpu_rows, seed=args.seed)
+        tflops, secs, desc = cpu_oracle_sample(w, rows=min(args.cpu_rows, w.M), seed=args.seed)
         cpu = {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
                "sample": desc, "seconds": round(secs, 2)}
 
