@@ -252,6 +252,31 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
                 dma4(o.sb, lds_addr(&sm.sb[s][0]), voff_s, (int)((int64_t)kb * p.ld_sb * 4));
         }
     };
+    // The same copies issued by the four waves of group g alone (rows
+    // [(4i + w % 4) * 8, +8) in round i = 0..7).  Copies stall the issuing
+    // wave while the CU's address unit works through them (about 1 KiB per
+    // 16 cycles); with one group issuing per K block, the other group's
+    // waves go straight to their MFMAs and keep the matrix pipes busy.
+    const int wq = w & 3;
+    const int voff_a4 = (int)((wq * 8 + ld_lrow) * p.lda) + ld_lchunk * 16;
+    const int voff_b4 = (int)((wq * 8 + ld_lrow) * p.ldb) + ld_lchunk * 16;
+    auto issue_loads_group = [&](const Operands& o, int32_t kb, int s, int g) {
+        if ((w >> 2) != g) return;
+        const int k_off = kb * BK;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            dma16(o.a, lds_addr(&sm.a[s][(4 * i + wq) * 1024]), voff_a4, k_off + (int)(32 * i * p.lda));
+            dma16(o.b, lds_addr(&sm.b[s][(4 * i + wq) * 1024]), voff_b4, k_off + (int)(32 * i * p.ldb));
+        }
+        if (wq == 0) {
+            dma16(o.sa, lds_addr(&sm.sa[s][0]), lane * 16, (int)((int64_t)kb * p.ld_sa * 4));
+        } else if (wq == 1) {
+            if (B1X128)
+                dma16(o.sb, lds_addr(&sm.sb[s][0]), voff_s, (int)((int64_t)kb * p.ld_sb * 4));
+            else if (lane < 2)
+                dma4(o.sb, lds_addr(&sm.sb[s][0]), voff_s, (int)((int64_t)kb * p.ld_sb * 4));
+        }
+    };
     auto frag = [&](const uint8_t* base, int row) -> v8i {
         const int sw = swz(row);
         const uint4 lo = *reinterpret_cast<const uint4*>(base + row * BK + (((2 * lg) ^ sw) * 16));
@@ -298,7 +323,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
 
         for (int32_t it = 0; it < nkb; ++it) {
             if (it + 1 < nkb) {
-                issue_loads(ops, cur.kb0 + it + 1, s ^ 1);
+                issue_loads_group(ops, cur.kb0 + it + 1, s ^ 1, it & 1);
             } else if (has_next) {
                 load_next(s ^ 1);
             }
