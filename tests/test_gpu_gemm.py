@@ -212,3 +212,86 @@ def test_group_k(sizes, out_dtype):
             assert ok, f"group {g}: worst {worst}"
         start = e
     assert torch.all(out_full[G] == 5.0)
+
+
+# ----------------------------------------------------------------------------
+# more tiles than workgroups: every workgroup walks several tiles, loading the
+# next tile's first K block during the current tile's last one
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", [bs.BS_SCALE_128X128, bs.BS_SCALE_1X128])
+def test_persistent_dense_many_tiles(kind):
+    need_gpu()
+    M, N, K = 4452, 4096, 256          # 18 x 16 = 288 tiles, ragged last tile row
+    qa, sa = operand_1x128(M, K, 1.0, seed=11)
+    if kind == bs.BS_SCALE_128X128:
+        qb, sb = operand_128x128(N, K, 0.02, seed=12)
+    else:
+        qb, sb = operand_1x128(N, K, 0.02, seed=12)
+    full, out = guarded(M, N, torch.bfloat16)
+    print(f"persistent dense {M}x{N}x{K} kind={kind}", flush=True)
+    bs.bs_scaled_mm(torch.from_numpy(qa).cuda(), to_gpu_scales(sa), torch.from_numpy(qb).cuda(),
+                    to_gpu_scales(sb), kind, out=out)
+    torch.cuda.synchronize()
+    check_result(out, qa, sa, qb, sb, 128 if kind == bs.BS_SCALE_128X128 else 1)
+    check_canaries(full, M, N)
+
+
+def test_persistent_group_m_many_tiles():
+    need_gpu()
+    sizes = (700, 0, 1300, 128, 0, 900, 601, 371)   # ragged and empty groups
+    G, N, K = len(sizes), 4096, 256                  # (tile rows = 21) x 16 = 336 tiles
+    ends = np.cumsum(sizes).astype(np.int32)
+    M = int(ends[-1])
+    qa, sa = operand_1x128(M, K, 1.0, seed=21)
+    w = inputs.bf16_normal((G * N, K), 0.02, seed=22)
+    qw, sw = quant.quant_128x128(bits16(w))
+    sw_gpu = to_gpu_scales(sw)
+    sb_view = torch.as_strided(sw_gpu, (G, K // 128, N // 128), (N // 128, sw_gpu.stride(0), 1))
+    full, out = guarded(M, N, torch.bfloat16)
+    print(f"persistent group_m sizes={sizes}", flush=True)
+    bs.bs_grouped_scaled_mm(bs.BS_GROUP_M, torch.from_numpy(ends).cuda(), torch.from_numpy(qa).cuda(),
+                            to_gpu_scales(sa), torch.from_numpy(qw).cuda().view(G, N, K), sb_view,
+                            bs.BS_SCALE_128X128, out=out)
+    torch.cuda.synchronize()
+    d = out.float().cpu().numpy().astype(np.float64)
+    start = 0
+    for g, e in enumerate(ends):
+        if e > start:
+            a = gemm.dequant(qa[start:e], sa[start:e], 1)
+            b = gemm.dequant(qw[g * N:(g + 1) * N], sw[g * N // 128:(g + 1) * N // 128], 128)
+            ok, worst = gemm.check_close(d[start:e], a @ b.T, a, b)
+            assert ok, f"group {g}: worst {worst}"
+        start = e
+    check_canaries(full, M, N)
+
+
+def test_persistent_group_k_many_tiles():
+    need_gpu()
+    # 20 groups of 16 tiles each (320 tiles); empty groups sit between
+    # non-empty ones, so workgroups pass through tiles with no K blocks
+    sizes = (256, 0, 128, 0, 0, 384, 128, 0, 256, 128, 0, 128, 0, 0, 256, 128, 0, 128, 0, 256)
+    G, M, N = len(sizes), 1024, 1024
+    ends = np.cumsum(sizes).astype(np.int32)
+    T = int(ends[-1])
+    qa, sa = operand_1x128(M, T, 0.01, seed=31)
+    qb, sb = operand_1x128(N, T, 1.0, seed=32)
+    out_full = torch.full((G + 1, M, N), 5.0, dtype=torch.float32, device="cuda")
+    out = out_full[:G]
+    print(f"persistent group_k G={G}", flush=True)
+    bs.bs_grouped_scaled_mm(bs.BS_GROUP_K, torch.from_numpy(ends).cuda(), torch.from_numpy(qa).cuda(),
+                            to_gpu_scales(sa), torch.from_numpy(qb).cuda(), to_gpu_scales(sb),
+                            bs.BS_SCALE_1X128, out=out)
+    torch.cuda.synchronize()
+    d = out.cpu().numpy().astype(np.float64)
+    start = 0
+    for g, e in enumerate(ends):
+        if e == start:
+            assert np.all(d[g] == 0), f"empty group {g} must be zeros"
+        else:
+            a = gemm.dequant(qa[:, start:e], sa[:, start // 128:e // 128], 1)
+            b = gemm.dequant(qb[:, start:e], sb[:, start // 128:e // 128], 1)
+            ok, worst = gemm.check_close(d[g], a @ b.T, a, b)
+            assert ok, f"group {g}: worst {worst}"
+        start = e
+    assert torch.all(out_full[G] == 5.0)
