@@ -22,3 +22,4 @@ from .binding import (  # noqa: F401
     bs_scaled_mm,
     empty_scales,
 )
+from .linear import Float8BlockwiseLinear, float8_blockwise_linear, swap_linear_layers  # noqa: F401,E402
