@@ -23,7 +23,8 @@
 //  * Persistent workgroups (one per CU) walk the tiles; the first K block
 //    of the next tile is loaded during the last K block of the current one,
 //    and the output tile is staged through LDS so that every store writes
-//    whole 128-byte rows while those loads land.
+//    whole 128-byte rows while those loads land.  Output stores are
+//    non-temporal.
 //  * Tile ids are remapped so that each of the 8 XCDs works on a contiguous
 //    range of tiles, ordered in groups of 8 tile rows for L2 reuse.
 #include "bs_kernels.h"
@@ -35,6 +36,7 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int NT = 512;
@@ -418,8 +420,12 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
                     const int row = q * RPI + rrow;
                     const uint4 v = *reinterpret_cast<const uint4*>(stg + row * PITCH + rch * 16);
                     const int64_t m = (int64_t)cur.m0 + wm * WM + i * 16 + row;
+                    // non-temporal: the output is not read again here, and
+                    // keeping it out of the caches leaves them to the operand
+                    // tiles (and to the inputs of whatever runs next)
                     if (m < cur.m_end && n < p.N)
-                        *reinterpret_cast<uint4*>(dbase + (m * p.ldd + n) * ESZ) = v;
+                        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v),
+                                                    reinterpret_cast<u32x4*>(dbase + (m * p.ldd + n) * ESZ));
                 }
                 // the next block's writes reuse the staging rows
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
