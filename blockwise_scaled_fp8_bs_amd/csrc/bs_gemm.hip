@@ -45,11 +45,15 @@ constexpr int WM = 128, WN = 64;
 constexpr int TM = WM / 16, TN = WN / 16;
 constexpr int kGroupRows = 8;  // tile rows per L2 group
 
+constexpr int kMaxRankedGroups = 256;  // GROUP_K: groups ordered by size up to this count (<= NT)
+
 struct __attribute__((aligned(16))) Smem {
     uint8_t a[2][BM * BK];
     uint8_t b[2][BN * BK];
     float sa[2][BM];
     float sb[2][BN];
+    int32_t group_by_rank[kMaxRankedGroups];  // GROUP_K: group index of the r-th largest group
+    int32_t group_tmp[kMaxRankedGroups];
 };
 
 __device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t n) {
@@ -98,11 +102,11 @@ __device__ __forceinline__ int64_t tile_total(const GemmArgs& p, int64_t& rows) 
 
 template <int KIND>
 __device__ __forceinline__ void resolve_tile(const GemmArgs& p, int64_t idx, int64_t total, int64_t rows,
-                                             Tile& t) {
+                                             const int32_t* group_by_rank, Tile& t) {
     t.g = 0;
     t.kb0 = 0;
     t.kb1 = (int32_t)(p.K / BK);
-    const int64_t L = xcd_remap(idx, total);
+    const int64_t L = KIND == kGroupK ? 0 : xcd_remap(idx, total);
     if (KIND == kDense) {
         int64_t tm, tn;
         grouped_order(L, p.tiles_m, p.tiles_n, tm, tn);
@@ -130,10 +134,24 @@ __device__ __forceinline__ void resolve_tile(const GemmArgs& p, int64_t idx, int
             prev = e;
         }
     } else {  // kGroupK
+        // Tiles of a group cost its K blocks, which differ widely between
+        // groups.  Logical order: groups by decreasing size (tiles of one
+        // group in the L2-grouped order); dealt round by round over the
+        // persistent workgroups, each XCD taking 32 consecutive tiles of a
+        // round, alternating direction between rounds (a workgroup that got
+        // one of a round's larger tiles gets a smaller one next).
         const int64_t per_g = p.tiles_m * p.tiles_n;
-        const int64_t g = L / per_g;
+        const int64_t nw = gridDim.x, round = idx / nw, slot = idx % nw;
+        int64_t Lk = idx;
+        if ((round + 1) * nw <= total) {  // full round: permute within it
+            int64_t pos = (nw % 8 == 0) ? (slot % 8) * (nw / 8) + slot / 8 : slot;
+            if (round & 1) pos = nw - 1 - pos;
+            Lk = round * nw + pos;
+        }
+        const int64_t rank = Lk / per_g;
+        const int64_t g = p.G <= kMaxRankedGroups ? group_by_rank[rank] : rank;
         int64_t tm, tn;
-        grouped_order(L % per_g, p.tiles_m, p.tiles_n, tm, tn);
+        grouped_order(Lk % per_g, p.tiles_m, p.tiles_n, tm, tn);
         int64_t s = 0, e = 0;
         for (int64_t h = 0; h <= g; ++h) {
             s = e;
@@ -227,6 +245,39 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
     int64_t idx = blockIdx.x;
     if (idx >= total) return;
 
+    if (KIND == kGroupK && p.G <= kMaxRankedGroups) {
+        // Rank the groups by size, largest first (ties: lower index first);
+        // thread g handles group g.  Sizes come from the clamped cumulative
+        // ends e_g = max(e_{g-1}, min(end_g, K)), e_{-1} = 0.
+        const int t0 = threadIdx.x;
+        if (t0 < p.G) {
+            const int64_t v = p.group_end[t0];
+            sm.group_tmp[t0] = (int32_t)(v < 0 ? 0 : (v > p.K ? p.K : v));
+        }
+        __syncthreads();
+        int32_t sz = 0;
+        if (t0 < p.G) {
+            int32_t e = 0, st = 0;
+            for (int h = 0; h <= t0; ++h) {
+                st = e;
+                e = sm.group_tmp[h] > e ? sm.group_tmp[h] : e;
+            }
+            sz = e - st;
+        }
+        __syncthreads();
+        if (t0 < p.G) sm.group_tmp[t0] = sz;
+        __syncthreads();
+        if (t0 < p.G) {
+            int r = 0;
+            for (int h = 0; h < p.G; ++h) {
+                const int32_t sh = sm.group_tmp[h];
+                r += (sh > sz || (sh == sz && h < t0)) ? 1 : 0;
+            }
+            sm.group_by_rank[r] = t0;
+        }
+        __syncthreads();
+    }
+
     // Wave w fills LDS rows [(8i + w) * 8, +8) of each operand in round i
     // (1 KiB: lane l -> physical chunk l % 8 of row l / 8, which holds the
     // logical chunk (l % 8) ^ swz(row); swz sees bits 0..3 of the row, i.e.
@@ -290,7 +341,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
     };
 
     Tile cur;
-    resolve_tile<KIND>(p, idx, total, rows_total, cur);
+    resolve_tile<KIND>(p, idx, total, rows_total, sm.group_by_rank, cur);
     Operands ops = make_operands<KIND, B1X128>(p, cur);
     int32_t nkb = cur.kb1 - cur.kb0;
     int s = 0;  // LDS stage holding the current K block
@@ -308,7 +359,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
         Operands nops = ops;
         bool next_resolved = false;
         auto load_next = [&](int stage) {
-            resolve_tile<KIND>(p, nidx, total, rows_total, nxt);
+            resolve_tile<KIND>(p, nidx, total, rows_total, sm.group_by_rank, nxt);
             nops = make_operands<KIND, B1X128>(p, nxt);
             if (nxt.kb1 > nxt.kb0) issue_loads(nops, nxt.kb0, stage);
             next_resolved = true;

@@ -295,3 +295,34 @@ def test_persistent_group_k_many_tiles():
             assert ok, f"group {g}: worst {worst}"
         start = e
     assert torch.all(out_full[G] == 5.0)
+
+
+def test_group_k_more_groups_than_ranked():
+    """GROUP_K with more groups than the kernel ranks by size (256): the
+    tiles then follow the natural group order."""
+    need_gpu()
+    rng = np.random.default_rng(41)
+    G, M, N = 300, 256, 256
+    sizes = np.where(rng.random(G) < 0.1, 128, 0)
+    sizes[[0, 7, 299]] = [256, 128, 384]
+    ends = np.cumsum(sizes).astype(np.int32)
+    T = int(ends[-1])
+    qa, sa = operand_1x128(M, T, 0.01, seed=42)
+    qb, sb = operand_1x128(N, T, 1.0, seed=43)
+    out = torch.full((G, M, N), 5.0, dtype=torch.bfloat16, device="cuda")
+    print(f"group_k G={G} T={T}", flush=True)
+    bs.bs_grouped_scaled_mm(bs.BS_GROUP_K, torch.from_numpy(ends).cuda(), torch.from_numpy(qa).cuda(),
+                            to_gpu_scales(sa), torch.from_numpy(qb).cuda(), to_gpu_scales(sb),
+                            bs.BS_SCALE_1X128, out=out)
+    torch.cuda.synchronize()
+    d = out.float().cpu().numpy().astype(np.float64)
+    start = 0
+    for g, e in enumerate(ends):
+        if e == start:
+            assert np.all(d[g] == 0), f"empty group {g} must be zeros"
+        else:
+            a = gemm.dequant(qa[:, start:e], sa[:, start // 128:e // 128], 1)
+            b = gemm.dequant(qb[:, start:e], sb[:, start // 128:e // 128], 1)
+            ok, worst = gemm.check_close(d[g], a @ b.T, a, b)
+            assert ok, f"group {g}: worst {worst}"
+        start = e
