@@ -4,7 +4,7 @@ One step = every kernel of one blockwise-FP8 linear layer's training pass
 over one batch of seeded synthetic data already resident in HBM:
 
   quantize A [M, K] rows + transposed columns (1x128),
-  quantize W [N, K] (128x128) and W^T (3-D colwise, G = 1),
+  quantize W [N, K] (128x128) and W^T (3-D colwise layout) in one pass,
   quantize grad_out [M, N] rows + transposed columns (1x128),
   forward  out     = A . W^T          (1x128 x 128x128),
   dgrad    grad_in = grad_out . W     (1x128 x 128x128, via W^T),
@@ -47,8 +47,7 @@ def r4(n):
 KERNEL_SYMBOL = {
     "quant_1x128_rowcol(A)": "quant_1x128_kernel<true, true>",
     "quant_1x128_rowcol(grad_out)": "quant_1x128_kernel<true, true>",
-    "quant_128x128(W)": "quant_128x128_kernel<false>",
-    "quant_3d_colwise(W)": "quant_128x128_kernel<true>",
+    "quant_128x128_both(W)": "quant_128x128_kernel<2>",
     "gemm_fwd": "gemm_kernel<0, false, false>",
     "gemm_dgrad": "gemm_kernel<0, false, false>",
     "gemm_wgrad": "gemm_kernel<0, true, false>",
@@ -130,13 +129,12 @@ class Step:
         M, K, N, G = w.M, w.K, w.N, w.G
         gemm_flops = 2.0 * M * N * K
         q1_bytes = lambda R, C: R * C * (2 + 2) + 4 * (R * C // 128) * 2  # noqa: E731
-        q128_bytes = lambda R, C: R * C * 3 + 4 * (R * C // 16384)  # noqa: E731
+        q128b_bytes = lambda R, C: R * C * (2 + 1 + 1) + 4 * (R * C // 16384) * 2  # noqa: E731
         ks = [
             ("quant_1x128_rowcol(A)", lambda: bs.bs_quant_1x128(self.a, self.qa, self.sa, self.qaT, self.saT),
              q1_bytes(M, K), "GB/s"),
-            ("quant_128x128(W)", lambda: bs.bs_quant_128x128(self.wv, self.qw, self.sw), q128_bytes(G * N, K), "GB/s"),
-            ("quant_3d_colwise(W)", lambda: bs.bs_quant_3d_colwise(self.w3, self.qwT, self.swT),
-             q128_bytes(G * N, K), "GB/s"),
+            ("quant_128x128_both(W)", lambda: bs.bs_quant_128x128_both(self.w3, self.qw, self.sw, self.qwT, self.swT),
+             q128b_bytes(G * N, K), "GB/s"),
             ("quant_1x128_rowcol(grad_out)",
              lambda: bs.bs_quant_1x128(self.gout, self.qg, self.sg, self.qgT, self.sgT), q1_bytes(M, N), "GB/s"),
         ]

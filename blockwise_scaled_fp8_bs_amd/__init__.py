@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     bs_diag_e4m3_census,
     bs_grouped_scaled_mm,
     bs_quant_128x128,
+    bs_quant_128x128_both,
     bs_quant_1x128,
     bs_quant_3d_colwise,
     bs_scaled_mm,

@@ -152,6 +152,31 @@ def bs_quant_3d_colwise(x, q, s, stream=None):
            "bs_quant_3d_colwise")
 
 
+def bs_quant_128x128_both(x, q, s, qt, st, stream=None):
+    """128x128 quantizer writing both weight layouts from one read of x.
+
+    x [G, R, C] bf16 (or [R, C] for G = 1);
+    q [G*R, C] uint8 with s [C/128, >= G*R/128]: the stacked forward layout;
+    qt [G, C, R] uint8 with st [G, R/128, >= C/128]: the transposed (dgrad) layout.
+    """
+    if x is not None and x.dim() == 2:
+        x = x.unsqueeze(0)
+    _mat(x, "x", torch.bfloat16, 3)
+    _mat(q, "q", torch.uint8)
+    _mat(qt, "qt", torch.uint8, 3)
+    _mat(st, "st", torch.float32, 3)
+    G, R, C = x.shape
+    _require(tuple(q.shape) == (G * R, C), f"q must be [{G * R}, {C}] (the experts stacked)")
+    ld_s = _scale(s, "s", C // 128, G * R // 128)
+    _require(tuple(qt.shape) == (G, C, R), f"qt must be [{G}, {C}, {R}]")
+    _require(st.shape[0] == G and st.shape[1] == R // 128 and st.shape[2] >= C // 128,
+             f"st must be [{G}, {R // 128}, >= {C // 128}]")
+    _check(_lib.load().bs_quant_128x128_both(_ptr(x), G, R, C, x.stride(0), _ld(x), _ptr(q), _ld(q), _ptr(s), ld_s,
+                                             _ptr(qt), qt.stride(0), _ld(qt), _ptr(st), st.stride(0), st.stride(1),
+                                             _stream(stream)),
+           "bs_quant_128x128_both")
+
+
 # ----------------------------------------------------------------------------
 # GEMMs
 # ----------------------------------------------------------------------------

@@ -121,7 +121,7 @@ bs_status bs_quant_128x128(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x
     REQUIRE(aligned16(s), BS_ERR_ALIGN, "s must be 16-byte aligned");
     if (R == 0 || C == 0) return ok();
     bs::Quant128Args a{x, 1, R, C, 0, ld_x, q, 0, ld_q, s, 0, ld_s, R / 128, C / 128};
-    return hip_status(bs::launch_quant_128x128(a, false, stream), fn);
+    return hip_status(bs::launch_quant_128x128(a, bs::kQ128Rows, stream), fn);
 }
 
 bs_status bs_quant_3d_colwise(const uint16_t* x, int64_t G, int64_t R, int64_t C, int64_t stride_xg, int64_t ld_x,
@@ -150,7 +150,47 @@ bs_status bs_quant_3d_colwise(const uint16_t* x, int64_t G, int64_t R, int64_t C
     REQUIRE(aligned16(s), BS_ERR_ALIGN, "s must be 16-byte aligned");
     if (G == 0 || R == 0 || C == 0) return ok();
     bs::Quant128Args a{x, G, R, C, stride_xg, ld_x, q, stride_qg, ld_q, s, stride_sg, ld_s, R / 128, C / 128};
-    return hip_status(bs::launch_quant_128x128(a, true, stream), fn);
+    return hip_status(bs::launch_quant_128x128(a, bs::kQ128Transposed, stream), fn);
+}
+
+bs_status bs_quant_128x128_both(const uint16_t* x, int64_t G, int64_t R, int64_t C, int64_t stride_xg,
+                                int64_t ld_x, uint8_t* q, int64_t ld_q, float* s, int64_t ld_s, uint8_t* qt,
+                                int64_t stride_qtg, int64_t ld_qt, float* st, int64_t stride_stg, int64_t ld_st,
+                                hipStream_t stream) {
+    static const char* fn = "bs_quant_128x128_both";
+    REQUIRE((x && q && s && qt && st) || G == 0 || R == 0 || C == 0, BS_ERR_NULL,
+            "x, q, s, qt and st must be non-NULL");
+    REQUIRE(G >= 0 && R >= 0 && C >= 0 && R % 128 == 0 && C % 128 == 0, BS_ERR_SHAPE,
+            "G=%lld R=%lld C=%lld: G >= 0 and R, C non-negative multiples of 128", (long long)G, (long long)R,
+            (long long)C);
+    REQUIRE(ld_x >= C, BS_ERR_LAYOUT, "ld_x=%lld < C=%lld: x[g] must be row-major [R, C]", (long long)ld_x,
+            (long long)C);
+    REQUIRE(G <= 1 || stride_xg >= R * ld_x, BS_ERR_LAYOUT, "stride_xg=%lld < R*ld_x", (long long)stride_xg);
+    REQUIRE(ld_q >= C, BS_ERR_LAYOUT, "ld_q=%lld < C=%lld: q is row-major [G*R, C]", (long long)ld_q, (long long)C);
+    REQUIRE(ld_s >= G * (R / 128), BS_ERR_LAYOUT,
+            "ld_s=%lld < G*R/128=%lld: s is K-major [C/128][ld_s >= G*R/128]", (long long)ld_s,
+            (long long)(G * (R / 128)));
+    REQUIRE(ld_s % 4 == 0, BS_ERR_LAYOUT, "ld_s=%lld must be a multiple of 4", (long long)ld_s);
+    REQUIRE(ld_qt >= R, BS_ERR_LAYOUT, "ld_qt=%lld < R=%lld: qt[g] is the transpose [C, R]", (long long)ld_qt,
+            (long long)R);
+    REQUIRE(G <= 1 || stride_qtg >= C * ld_qt, BS_ERR_LAYOUT, "stride_qtg=%lld < C*ld_qt", (long long)stride_qtg);
+    REQUIRE(ld_st >= C / 128, BS_ERR_LAYOUT, "ld_st=%lld < C/128=%lld: st[g] is K-major [R/128][ld_st >= C/128]",
+            (long long)ld_st, (long long)(C / 128));
+    REQUIRE(ld_st % 4 == 0, BS_ERR_LAYOUT, "ld_st=%lld must be a multiple of 4", (long long)ld_st);
+    REQUIRE(G <= 1 || stride_stg >= (R / 128) * ld_st, BS_ERR_LAYOUT, "stride_stg=%lld < (R/128)*ld_st",
+            (long long)stride_stg);
+    REQUIRE(stride_stg % 4 == 0 && stride_qtg % 16 == 0 && stride_xg % 8 == 0, BS_ERR_ALIGN,
+            "group strides must keep 16-byte alignment (stride_stg %% 4, stride_qtg %% 16, stride_xg %% 8)");
+    REQUIRE(aligned16(x) && ld_x % 8 == 0, BS_ERR_ALIGN, "x must be 16-byte aligned with ld_x %% 8 == 0");
+    REQUIRE(aligned16(q) && ld_q % 16 == 0, BS_ERR_ALIGN, "q must be 16-byte aligned with ld_q %% 16 == 0");
+    REQUIRE(aligned16(qt) && ld_qt % 16 == 0, BS_ERR_ALIGN, "qt must be 16-byte aligned with ld_qt %% 16 == 0");
+    REQUIRE(aligned16(s) && aligned16(st), BS_ERR_ALIGN, "s and st must be 16-byte aligned");
+    if (G == 0 || R == 0 || C == 0) return ok();
+    // rows of expert g are rows g*R .. of the stacked q; its scale columns
+    // start at g*R/128 of each K-major row of s
+    bs::Quant128Args a{x, G, R, C, stride_xg, ld_x, q, R * ld_q, ld_q, s, R / 128, ld_s, R / 128, C / 128,
+                       qt, stride_qtg, ld_qt, st, stride_stg, ld_st};
+    return hip_status(bs::launch_quant_128x128(a, bs::kQ128Both, stream), fn);
 }
 
 namespace {

@@ -5,7 +5,7 @@
 //
 // (pages: "[not for land] float8 blockwise scaling training prototype using
 // deep_gemm", description -- forward/backward GEMMs with 1x128 activation and
-// 128x128 weight scales, and the "1x128 by 1x128" grad_weight GEMM; "add FSDP
+// 128x128 weight scales, and the 1x128 x 1x128 grad_weight GEMM; "add FSDP
 // and TP tests for Float8BlockwiseLinear", review threads -- both operands
 // contiguous along the contraction, fp32 K-major scales.)
 //

@@ -29,7 +29,15 @@ struct Quant128Args {
     float* s;
     int64_t stride_sg, ld_s;
     int64_t row_tiles, col_tiles;  // R / 128, C / 128
+    // second (transposed) output of the fused pass: qt[g] [C, R], st[g] [R/128][ld_st]
+    uint8_t* qt;
+    int64_t stride_qtg, ld_qt;
+    float* st;
+    int64_t stride_stg, ld_st;
 };
+
+// Which outputs a 128x128 pass writes.
+enum Quant128Mode { kQ128Rows = 0, kQ128Transposed = 1, kQ128Both = 2 };
 
 enum GroupKind { kDense = 0, kGroupM = 1, kGroupK = 2 };
 
@@ -55,7 +63,7 @@ struct GemmArgs {
 };
 
 hipError_t launch_quant_1x128(const Quant1x128Args& a, bool row, bool col, hipStream_t stream);
-hipError_t launch_quant_128x128(const Quant128Args& a, bool transpose, hipStream_t stream);
+hipError_t launch_quant_128x128(const Quant128Args& a, Quant128Mode mode, hipStream_t stream);
 
 // b_1x128: B scales per row (wgrad) instead of per 128x128 block.
 hipError_t launch_gemm(const GemmArgs& a, GroupKind kind, bool b_1x128, bool out_f32, hipStream_t stream);

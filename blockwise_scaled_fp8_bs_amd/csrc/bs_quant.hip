@@ -194,9 +194,13 @@ __global__ __launch_bounds__(kThreads) void quant_1x128_kernel(Quant1x128Args a)
     }
 }
 
-// 128x128 quantizer; TRANSPOSE writes the tile transposed (3-D colwise).
-template <bool TRANSPOSE>
+// 128x128 quantizer.  MODE kQ128Rows writes the codes in place (q, s),
+// kQ128Transposed writes each tile transposed (3-D colwise: q, s), kQ128Both
+// writes both from one read of x (rows to q, s; transposed to qt, st).
+template <int MODE>
 __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(Quant128Args a) {
+    constexpr bool ROWS = MODE != kQ128Transposed;
+    constexpr bool TRANSPOSE = MODE != kQ128Rows;
     __shared__ float s_wmax[2][4];
     __shared__ __attribute__((aligned(16))) uint8_t s_tr[TRANSPOSE ? 2 : 1][TRANSPOSE ? kTile * kTile : 16];
 
@@ -247,8 +251,8 @@ __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(Quant128Args a)
                                  fmaxf(s_wmax[parity][2], s_wmax[parity][3]));
         const Scale sc = block_scale(amax);
 
-        uint8_t* q = a.q + g * a.stride_qg;
-        if (!TRANSPOSE) {
+        if (ROWS) {
+            uint8_t* q = a.q + g * a.stride_qg;
             const __amdgpu_buffer_rsrc_t rq = rsrc(q + r0 * a.ld_q + c0, (kTile - 1) * a.ld_q + kTile);
             const int voff_q = (8 * tr) * (int)a.ld_q + 8 * tc;
 #pragma unroll
@@ -257,14 +261,19 @@ __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(Quant128Args a)
                 __builtin_amdgcn_raw_buffer_store_b64(u32x2{c8.x, c8.y}, rq, voff_q, i * (int)a.ld_q, 0);
             }
             if (t == 0) a.s[g * a.stride_sg + ct * a.ld_s + rt] = sc.s;
-        } else {
+        }
+        if (TRANSPOSE) {
+            uint8_t* const qt = MODE == kQ128Both ? a.qt + g * a.stride_qtg : a.q + g * a.stride_qg;
+            float* const st = MODE == kQ128Both ? a.st + g * a.stride_stg : a.s + g * a.stride_sg;
+            const int64_t ld_qt = MODE == kQ128Both ? a.ld_qt : a.ld_q;
+            const int64_t ld_st = MODE == kQ128Both ? a.ld_st : a.ld_s;
             Scale scs[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) scs[j] = sc;
             uint2 codes[8];
             col_codes(tl, scs, codes);
-            if (t == 0) a.s[g * a.stride_sg + rt * a.ld_s + ct] = sc.s;
-            store_transposed(s_tr[parity], codes, tr, tc, q + c0 * a.ld_q + r0, a.ld_q);
+            if (t == 0) st[rt * ld_st + ct] = sc.s;
+            store_transposed(s_tr[parity], codes, tr, tc, qt + c0 * ld_qt + r0, ld_qt);
         }
     }
 }
@@ -301,11 +310,12 @@ hipError_t launch_quant_1x128(const Quant1x128Args& a, bool row, bool col, hipSt
     return launch_persistent(quant_1x128_kernel<false, true>, a, tiles, stream);
 }
 
-hipError_t launch_quant_128x128(const Quant128Args& a, bool transpose, hipStream_t stream) {
+hipError_t launch_quant_128x128(const Quant128Args& a, Quant128Mode mode, hipStream_t stream) {
     const int64_t tiles = a.G * a.row_tiles * a.col_tiles;
     if (tiles == 0) return hipSuccess;
-    if (transpose) return launch_persistent(quant_128x128_kernel<true>, a, tiles, stream);
-    return launch_persistent(quant_128x128_kernel<false>, a, tiles, stream);
+    if (mode == kQ128Both) return launch_persistent(quant_128x128_kernel<kQ128Both>, a, tiles, stream);
+    if (mode == kQ128Transposed) return launch_persistent(quant_128x128_kernel<kQ128Transposed>, a, tiles, stream);
+    return launch_persistent(quant_128x128_kernel<kQ128Rows>, a, tiles, stream);
 }
 
 }  // namespace bs

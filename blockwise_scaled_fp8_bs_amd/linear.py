@@ -8,17 +8,17 @@ run in FP8 with blockwise scales.)
 For y = x W^T with x [M, K] and W [N, K] (bf16):
 
   forward   q(x) 1x128 along K (rows), and along M (transposed, kept for wgrad)
-            q(W) 128x128
+            q(W) 128x128, and the same blocks written transposed (q(W^T) [K, N],
+            kept for dgrad), in one pass
             y        = scaled_mm(q(x), q(W))                     [M, N]
   backward  q(dy) 1x128 along N (rows) and along M (transposed)
-            q(W^T) 128x128 blocks of W written transposed       [K, N]
             dx       = scaled_mm(q(dy), q(W^T))                  [M, K]
             dW       = scaled_mm(q(dy^T), q(x^T)), both 1x128    [N, K]
 
 Every step runs in the HIP kernels; this module allocates outputs with torch
-and wires the calls into autograd.  The forward keeps only the transposed
-FP8 codes and scales of x (about half the bytes of the bf16 input) and a
-reference to W.  M, K and N must be multiples of 128 (the colwise blocks run
+and wires the calls into autograd.  The forward keeps only FP8 codes and
+scales for the backward: the transposed codes of x (about half the bytes of
+the bf16 input) and those of W^T.  M, K and N must be multiples of 128 (the colwise blocks run
 along M); inputs must be contiguous bf16 GPU tensors -- nothing is copied
 behind the caller's back.
 """
@@ -51,28 +51,29 @@ class _Float8BlockwiseLinearFn(torch.autograd.Function):
         M, K = x2.shape
         N = w.shape[0]
         qx, sx, qxt, sxt = _quant_rows_cols(x2)
+        # W in both layouts from one pass: rows for this GEMM, transposed
+        # (W^T, contiguous along N) kept for the dgrad GEMM
         qw = torch.empty((N, K), dtype=torch.uint8, device=w.device)
         sw = _b.empty_scales(K // 128, N // 128, w.device)
-        _b.bs_quant_128x128(w, qw, sw)
+        qwt = torch.empty((1, K, N), dtype=torch.uint8, device=w.device)
+        swt = torch.empty((1, N // 128, _b._round4(K // 128)), dtype=torch.float32, device=w.device)
+        _b.bs_quant_128x128_both(w, qw, sw, qwt, swt)
         y = _b.bs_scaled_mm(qx, sx, qw, sw, _b.BS_SCALE_128X128, out_dtype=torch.bfloat16)
-        ctx.save_for_backward(qxt, sxt, w)
+        ctx.save_for_backward(qxt, sxt, qwt, swt)
+        ctx.w_dtype = w.dtype
         return y
 
     @staticmethod
     def backward(ctx, dy):
-        qxt, sxt, w = ctx.saved_tensors
-        N, K = w.shape
+        qxt, sxt, qwt, swt = ctx.saved_tensors
         # autograd may hand a non-contiguous gradient; the kernels need rows
         dy = dy.to(torch.bfloat16).contiguous()
         qg, sg, qgt, sgt = _quant_rows_cols(dy)
         dx = dw = None
         if ctx.needs_input_grad[0]:
-            qwt = torch.empty((1, K, N), dtype=torch.uint8, device=w.device)
-            swt = torch.empty((1, N // 128, _b._round4(K // 128)), dtype=torch.float32, device=w.device)
-            _b.bs_quant_3d_colwise(w.unsqueeze(0), qwt, swt)
             dx = _b.bs_scaled_mm(qg, sg, qwt[0], swt[0], _b.BS_SCALE_128X128, out_dtype=torch.bfloat16)
         if ctx.needs_input_grad[1]:
-            dw = _b.bs_scaled_mm(qgt, sgt, qxt, sxt, _b.BS_SCALE_1X128, out_dtype=w.dtype)
+            dw = _b.bs_scaled_mm(qgt, sgt, qxt, sxt, _b.BS_SCALE_1X128, out_dtype=ctx.w_dtype)
         return dx, dw
 
 

@@ -30,10 +30,10 @@
  *     be NULL only when the tensor it points to has no elements.
  *   - Matrices are row-major with unit stride along the last dimension:
  *     element (i, j) of X is X[i * ld + j].  Both GEMM operands are
- *     contiguous along the contraction dimension ("A row-major, B
- *     column-major", "add FSDP and TP tests for Float8BlockwiseLinear",
- *     review thread on the layout assertions).
- *   - Scales are "K-major" (same page, review thread on
+ *     contiguous along the contraction dimension (A stored by rows, B by
+ *     columns: "add FSDP and TP tests for Float8BlockwiseLinear", review
+ *     thread on the layout assertions).
+ *   - Scales are K-major (same page, review thread on
  *     _pad_blockwise_128x128_scale_k_major): the contraction-block index is
  *     the outer index and the row (1x128) or row-block (128x128) index is
  *     contiguous, s[kb * ld_s + row] or s[kb * ld_s + row / 128], and ld_s is
@@ -121,10 +121,10 @@ bs_status bs_quant_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x,
  *   x [R, C] bf16 (R = out features, C = in features = contraction),
  *   q[r * ld_q + c], s[(c / 128) * ld_s + r / 128].
  *   R % 128 == 0, C % 128 == 0, ld_x >= C, ld_q >= C, ld_s >= R / 128.
- * Pages: prototype page, description ("128x128 scaling of a single tensor ...
- * 3 kernels per tensor"; "a fast version of 128x128 scaling ... with a
- * handwritten kernel"); "add FSDP and TP tests ...", review thread on the
- * K-major scale padding.
+ * Pages: prototype page, description (written with torch ops, 128x128
+ * scaling of one tensor takes three kernels, and a hand-written single
+ * kernel is the proposed fix); "add FSDP and TP tests ...", review thread on
+ * the K-major scale padding.
  */
 bs_status bs_quant_128x128(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x,
                            uint8_t* q, int64_t ld_q, float* s, int64_t ld_s,
@@ -153,6 +153,29 @@ bs_status bs_quant_3d_colwise(const uint16_t* x, int64_t G, int64_t R, int64_t C
                               hipStream_t stream);
 
 /*
+ * bs_quant_128x128_both -- bs_quant_128x128 and bs_quant_3d_colwise of the
+ * same weights in one pass (one read of x; the two outputs hold the same
+ * codes and scales, in the forward and the dgrad layouts).  For expert g of
+ * x[G][R][C] (x[g] at x + g * stride_xg):
+ *   rows, as one stacked [G*R, C] matrix (what the forward / GROUP_M GEMM
+ *   reads):  q[(g*R + r) * ld_q + c],  s[(c/128) * ld_s + g*R/128 + r/128]
+ *   transposed, per expert (what the dgrad GEMM reads):
+ *            qt[g * stride_qtg + c * ld_qt + r],
+ *            st[g * stride_stg + (r/128) * ld_st + c/128]
+ * G >= 0, R % 128 == 0, C % 128 == 0; ld_x >= C, stride_xg >= R*ld_x;
+ * ld_q >= C, ld_s >= G*R/128; ld_qt >= R, stride_qtg >= C*ld_qt;
+ * ld_st >= C/128, stride_stg >= (R/128)*ld_st; ld_s, ld_st multiples of 4.
+ * Pages: as for the two calls it fuses; the prototype page, description,
+ * proposes a single hand-written kernel for 128x128 scaling.
+ */
+bs_status bs_quant_128x128_both(const uint16_t* x, int64_t G, int64_t R, int64_t C,
+                                int64_t stride_xg, int64_t ld_x,
+                                uint8_t* q, int64_t ld_q, float* s, int64_t ld_s,
+                                uint8_t* qt, int64_t stride_qtg, int64_t ld_qt,
+                                float* st, int64_t stride_stg, int64_t ld_st,
+                                hipStream_t stream);
+
+/*
  * bs_scaled_mm -- D[M, N] = sum_kb sa(m, kb) * sb(n, kb) * P_kb[m, n],
  * P_kb = sum over k in block kb of dec(a[m][k]) * dec(b[n][k]) (fp32 MFMA),
  * accumulated in fp32 and written as bf16 (nearest-even) or fp32.
@@ -160,7 +183,7 @@ bs_status bs_quant_3d_colwise(const uint16_t* x, int64_t G, int64_t R, int64_t C
  * threads (blockwise_scaled_mm(a, scale_a, scale_recipe_a, b, scale_b,
  * scale_recipe_b); one scale layout; fail loudly on wrong layouts);
  * prototype page, description (fwd and bwd GEMMs of a dense linear; the
- * "1x128 by 1x128" grad_weight GEMM).
+ * 1x128 x 1x128 grad_weight GEMM).
  *
  *   a  [M, K] e4m3, lda >= K;  sa 1x128: sa[(k/128) * ld_sa + m], ld_sa >= M.
  *      a_kind must be BS_SCALE_1X128.
@@ -184,8 +207,8 @@ bs_status bs_scaled_mm(int64_t M, int64_t N, int64_t K,
 
 /*
  * bs_grouped_scaled_mm -- the MoE form of bs_scaled_mm (pages: prototype page,
- * description, "fwd and bwd grouped gemms for MoE"; "[mxfp8 moe training]
- * ...", microbenchmark table, shapes (M, N, K, G)).
+ * description, which lists grouped forward and backward GEMMs for MoE;
+ * "[mxfp8 moe training] ...", microbenchmark table, shapes (M, N, K, G)).
  *
  * group_end: DEVICE int32[G], cumulative ends of the G groups along the
  * grouped axis, non-decreasing, last == the axis length; zero-size groups are

@@ -153,3 +153,30 @@ def test_grouped_validation(lib):
     assert call(mode=1, b_kind=4, ld_sb=256, sbg=0, ssbg=0, sdg=10) == LAYOUT
     assert call(mode=1, b_kind=4, ld_sb=256, sbg=0, ssbg=0, sdg=256 * 256, G=0) == OK
     assert call(mode=1, b_kind=4, ld_sb=256, sbg=7, ssbg=0, sdg=256 * 256) == MODE
+
+
+def _q128b(lib, x=P, G=2, R=256, C=384, stride_xg=256 * 384, ld_x=384, q=P, ld_q=384, s=P, ld_s=4,
+           qt=P, stride_qtg=384 * 256, ld_qt=256, st=P, stride_stg=2 * 4, ld_st=4):
+    return lib.bs_quant_128x128_both(x, G, R, C, stride_xg, ld_x, q, ld_q, s, ld_s, qt, stride_qtg, ld_qt, st,
+                                     stride_stg, ld_st, None)
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(qt=None), NULL, "non-NULL"),
+    (dict(R=200), SHAPE, "multiples of 128"),
+    (dict(ld_q=256), LAYOUT, "ld_q"),
+    (dict(ld_s=2), LAYOUT, "ld_s"),        # G*R/128 = 4 scale columns needed
+    (dict(ld_s=6), LAYOUT, "multiple of 4"),
+    (dict(ld_qt=128), LAYOUT, "ld_qt"),
+    (dict(stride_qtg=1000), LAYOUT, "stride_qtg"),
+    (dict(stride_stg=4), LAYOUT, "stride_stg"),
+    (dict(stride_xg=100), LAYOUT, "stride_xg"),
+    (dict(q=PU), ALIGN, "q must be 16-byte aligned"),
+])
+def test_quant_128x128_both_validation(lib, kw, code, frag):
+    assert _q128b(lib, **kw) == code
+    assert frag in lib.bs_last_error().decode()
+
+
+def test_quant_128x128_both_empty_is_ok(lib):
+    assert _q128b(lib, G=0, x=None, q=None, s=None, qt=None, st=None) == OK

@@ -117,6 +117,48 @@ def test_quant_3d_colwise(G, R, C):
     assert np.all(sg[:G, :, C // 128:] == 0x7FBADBAD) and np.all(sg[G:] == 0x7FBADBAD)
 
 
+@pytest.mark.parametrize("G,R,C,xpad", [(1, 384, 640, 0), (3, 256, 384, 128), (2, 128, 896, 0)])
+def test_quant_128x128_both(G, R, C, xpad):
+    """The fused pass writes exactly what bs_quant_128x128 on the stacked
+    weights and bs_quant_3d_colwise write (oracle codes and scales)."""
+    need_gpu()
+    x = torch.stack([special_input(R, C, seed=g * 13 + C, sigma=0.02) for g in range(G)])
+    xs = torch.zeros((G, R + xpad // 128 * 128, C + 16), dtype=torch.bfloat16)
+    xs[:, :R, :C] = x
+    xg = xs.cuda()[:, :R, :C]                      # strided experts and rows
+    ld_s = (G * R // 128 + 3) // 4 * 4 + 4
+    q_full = torch.full((G * R + 1, C + 16), 0xA5, dtype=torch.uint8, device="cuda")
+    q = q_full[:G * R, :C]
+    s_full = torch.empty((C // 128 + 1, ld_s), dtype=torch.float32, device="cuda")
+    s_full.view(torch.int32).fill_(0x7FBADBAD)
+    s = s_full[:C // 128]
+    ld_st = (C // 128 + 3) // 4 * 4 + 4
+    qt_full = torch.full((G + 1, C, R + 16), 0xA5, dtype=torch.uint8, device="cuda")
+    qt = qt_full[:G, :, :R]
+    st_full = torch.empty((G + 1, R // 128, ld_st), dtype=torch.float32, device="cuda")
+    st_full.view(torch.int32).fill_(0x7FBADBAD)
+    st = st_full[:G]
+    print(f"quant_128x128_both G={G} R={R} C={C}", flush=True)
+    bs.bs_quant_128x128_both(xg, q, s, qt, st)
+    torch.cuda.synchronize()
+    xb = bits16(x)
+    q_ref, s_ref = quant.quant_128x128(xb.reshape(G * R, C))
+    qt_ref, st_ref = quant.quant_3d_colwise(xb)
+    qa = u8(q_full)
+    assert np.array_equal(qa[:G * R, :C], q_ref)
+    assert np.all(qa[:G * R, C:] == 0xA5) and np.all(qa[G * R:] == 0xA5)
+    sa = s_full.cpu().view(torch.int32).numpy().view(np.uint32)
+    assert np.array_equal(sa[:C // 128, :G * R // 128], np.ascontiguousarray(s_ref.T).view(np.uint32))
+    assert np.all(sa[:C // 128, G * R // 128:] == 0x7FBADBAD) and np.all(sa[C // 128:] == 0x7FBADBAD)
+    qta = u8(qt_full)
+    assert np.array_equal(qta[:G, :, :R], qt_ref)
+    assert np.all(qta[:G, :, R:] == 0xA5) and np.all(qta[G:] == 0xA5)
+    sta = st_full.cpu().view(torch.int32).numpy().view(np.uint32)
+    for g in range(G):
+        assert np.array_equal(sta[g, :, :C // 128], np.ascontiguousarray(st_ref[g].T).view(np.uint32))
+    assert np.all(sta[:G, :, C // 128:] == 0x7FBADBAD) and np.all(sta[G:] == 0x7FBADBAD)
+
+
 def test_quant_division_not_reciprocal():
     """Blocks where x * fl32(1/s) and fl32(x / s) give different codes."""
     need_gpu()
