@@ -9,6 +9,10 @@
 
 namespace {
 
+// Leading dimensions (elements) stay below 2^22 so that the kernels' lane
+// and in-tile offsets (up to 256 rows of a tile) fit in 32 bits.
+constexpr int64_t kMaxLd = (int64_t)1 << 22;
+
 thread_local std::string g_last_error;
 
 bs_status fail(bs_status st, const char* fn, const char* fmt, ...) {
@@ -75,6 +79,7 @@ bs_status bs_quant_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x, 
             "R=%lld must be a multiple of 128 for the column output (128-row blocks)", (long long)R);
     REQUIRE(ld_x >= C, BS_ERR_LAYOUT, "ld_x=%lld < C=%lld: x must be row-major [R, C]", (long long)ld_x,
             (long long)C);
+    REQUIRE(ld_x < kMaxLd, BS_ERR_LAYOUT, "ld_x=%lld must be < 2^22 (32-bit offsets inside a tile)", (long long)ld_x);
     REQUIRE(aligned16(x) && ld_x % 8 == 0, BS_ERR_ALIGN, "x must be 16-byte aligned with ld_x %% 8 == 0");
     if (row) {
         REQUIRE(ld_qr >= C, BS_ERR_LAYOUT, "ld_qr=%lld < C=%lld: q_row is row-major [R, C]", (long long)ld_qr,
@@ -83,6 +88,7 @@ bs_status bs_quant_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x, 
                 (long long)ld_sr, (long long)R);
         REQUIRE(ld_sr % 4 == 0, BS_ERR_LAYOUT, "ld_sr=%lld must be a multiple of 4 (16-byte scale rows)",
                 (long long)ld_sr);
+        REQUIRE(ld_qr < kMaxLd, BS_ERR_LAYOUT, "ld_qr=%lld must be < 2^22", (long long)ld_qr);
         REQUIRE(aligned16(q_row) && ld_qr % 16 == 0, BS_ERR_ALIGN,
                 "q_row must be 16-byte aligned with ld_qr %% 16 == 0");
         REQUIRE(aligned16(s_row), BS_ERR_ALIGN, "s_row must be 16-byte aligned");
@@ -94,6 +100,7 @@ bs_status bs_quant_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x, 
                 (long long)ld_sc, (long long)C);
         REQUIRE(ld_sc % 4 == 0, BS_ERR_LAYOUT, "ld_sc=%lld must be a multiple of 4 (16-byte scale rows)",
                 (long long)ld_sc);
+        REQUIRE(ld_qc < kMaxLd, BS_ERR_LAYOUT, "ld_qc=%lld must be < 2^22", (long long)ld_qc);
         REQUIRE(aligned16(q_col) && ld_qc % 16 == 0, BS_ERR_ALIGN,
                 "q_col must be 16-byte aligned with ld_qc %% 16 == 0");
         REQUIRE(aligned16(s_col), BS_ERR_ALIGN, "s_col must be 16-byte aligned");
@@ -116,6 +123,8 @@ bs_status bs_quant_128x128(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x
             (long long)ld_s, (long long)(R / 128));
     REQUIRE(ld_s % 4 == 0, BS_ERR_LAYOUT, "ld_s=%lld must be a multiple of 4 (K stride padded to 16 bytes)",
             (long long)ld_s);
+    REQUIRE(ld_x < kMaxLd, BS_ERR_LAYOUT, "ld_x=%lld must be < 2^22 (32-bit offsets inside a tile)", (long long)ld_x);
+    REQUIRE(ld_q < kMaxLd, BS_ERR_LAYOUT, "ld_q=%lld must be < 2^22", (long long)ld_q);
     REQUIRE(aligned16(x) && ld_x % 8 == 0, BS_ERR_ALIGN, "x must be 16-byte aligned with ld_x %% 8 == 0");
     REQUIRE(aligned16(q) && ld_q % 16 == 0, BS_ERR_ALIGN, "q must be 16-byte aligned with ld_q %% 16 == 0");
     REQUIRE(aligned16(s), BS_ERR_ALIGN, "s must be 16-byte aligned");
@@ -145,6 +154,8 @@ bs_status bs_quant_3d_colwise(const uint16_t* x, int64_t G, int64_t R, int64_t C
             (long long)stride_sg);
     REQUIRE(stride_sg % 4 == 0 && stride_qg % 16 == 0 && stride_xg % 8 == 0, BS_ERR_ALIGN,
             "group strides must keep 16-byte alignment (stride_sg %% 4, stride_qg %% 16, stride_xg %% 8)");
+    REQUIRE(ld_x < kMaxLd, BS_ERR_LAYOUT, "ld_x=%lld must be < 2^22 (32-bit offsets inside a tile)", (long long)ld_x);
+    REQUIRE(ld_q < kMaxLd, BS_ERR_LAYOUT, "ld_q=%lld must be < 2^22", (long long)ld_q);
     REQUIRE(aligned16(x) && ld_x % 8 == 0, BS_ERR_ALIGN, "x must be 16-byte aligned with ld_x %% 8 == 0");
     REQUIRE(aligned16(q) && ld_q % 16 == 0, BS_ERR_ALIGN, "q must be 16-byte aligned with ld_q %% 16 == 0");
     REQUIRE(aligned16(s), BS_ERR_ALIGN, "s must be 16-byte aligned");
@@ -181,6 +192,9 @@ bs_status bs_quant_128x128_both(const uint16_t* x, int64_t G, int64_t R, int64_t
             (long long)stride_stg);
     REQUIRE(stride_stg % 4 == 0 && stride_qtg % 16 == 0 && stride_xg % 8 == 0, BS_ERR_ALIGN,
             "group strides must keep 16-byte alignment (stride_stg %% 4, stride_qtg %% 16, stride_xg %% 8)");
+    REQUIRE(ld_x < kMaxLd, BS_ERR_LAYOUT, "ld_x=%lld must be < 2^22 (32-bit offsets inside a tile)", (long long)ld_x);
+    REQUIRE(ld_q < kMaxLd && ld_qt < kMaxLd, BS_ERR_LAYOUT, "ld_q=%lld and ld_qt=%lld must be < 2^22",
+            (long long)ld_q, (long long)ld_qt);
     REQUIRE(aligned16(x) && ld_x % 8 == 0, BS_ERR_ALIGN, "x must be 16-byte aligned with ld_x %% 8 == 0");
     REQUIRE(aligned16(q) && ld_q % 16 == 0, BS_ERR_ALIGN, "q must be 16-byte aligned with ld_q %% 16 == 0");
     REQUIRE(aligned16(qt) && ld_qt % 16 == 0, BS_ERR_ALIGN, "qt must be 16-byte aligned with ld_qt %% 16 == 0");

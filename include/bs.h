@@ -25,6 +25,9 @@
  *
  * Conventions for every entry point
  *   - Dimensions and leading dimensions ("ld") are in ELEMENTS, int64_t.
+ *     Leading dimensions of data matrices (bf16 inputs, e4m3 codes, GEMM
+ *     operands) must be < 2^22: the kernels address within a tile with
+ *     32-bit offsets.  Larger values are rejected with BS_ERR_LAYOUT.
  *   - bf16 tensors are passed as uint16_t bit patterns, e4m3 codes as uint8_t,
  *     scales as float.  All data pointers are DEVICE pointers.  A pointer may
  *     be NULL only when the tensor it points to has no elements.

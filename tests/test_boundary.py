@@ -180,3 +180,12 @@ def test_quant_128x128_both_validation(lib, kw, code, frag):
 
 def test_quant_128x128_both_empty_is_ok(lib):
     assert _q128b(lib, G=0, x=None, q=None, s=None, qt=None, st=None) == OK
+
+
+def test_leading_dimensions_are_bounded(lib):
+    big = 1 << 22
+    assert _q1(lib, ld_x=big) == LAYOUT and b"ld_x" in lib.bs_last_error()
+    assert _q1(lib, ld_qr=big) == LAYOUT and b"ld_qr" in lib.bs_last_error()
+    assert lib.bs_quant_128x128(P, 256, 512, 512, P, big, P, 4, None) == LAYOUT
+    assert _q128b(lib, ld_x=big, stride_xg=256 * big) == LAYOUT
+    assert _q128b(lib, ld_qt=big, stride_qtg=384 * big) == LAYOUT
