@@ -59,11 +59,23 @@ KERNEL_SYMBOL = {
 }
 
 
-def kernel_source_hash():
+# sources each device kernel is built from (a counter summary stays valid
+# while these are unchanged)
+KERNEL_SOURCES = {
+    "gemm_kernel": ["bs_gemm.hip", "bs_kernels.h"],
+    "quant_": ["bs_quant.hip", "bs_device.h", "bs_kernels.h"],
+}
+
+
+def kernel_source_hash(symbol):
+    """sha256 prefix of the sources of the device kernel `symbol`."""
     import hashlib
     src = os.path.join(ROOT, "blockwise_scaled_fp8_bs_amd", "csrc")
+    files = next((fs for prefix, fs in KERNEL_SOURCES.items() if symbol.startswith(prefix)), None)
+    if files is None:
+        return None
     h = hashlib.sha256()
-    for f in sorted(os.listdir(src)):
+    for f in files:
         h.update(open(os.path.join(src, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -77,7 +89,7 @@ def counter_traffic(workload, kernel):
     if not os.path.exists(path):
         return None
     sym = KERNEL_SYMBOL.get(kernel)
-    cur = kernel_source_hash()
+    cur = kernel_source_hash(sym) if sym else None
     for line in open(path):
         if line.startswith("traffic_bytes ") and sym and sym in line:
             fields = line.split()
