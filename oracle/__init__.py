@@ -17,6 +17,8 @@ What it computes (plain numpy, slow on purpose):
 * ``gemm``   -- the blockwise-scaled matmuls as "dequantize to float64, then
   float64 matmul", dense and grouped, plus the per-element tolerance of the
   parity bar.
+* ``swiglu`` -- the gated FFN activation silu(a) * b rounded once to bf16
+  (what the fused activation-and-quantize kernel quantizes).
 
 Sources: the three pytorch/ao pull-request pages on blockwise FP8 training
 ("[not for land] float8 blockwise scaling training prototype using
@@ -31,4 +33,4 @@ reading the pages cannot decide -- the block shape of the 3-D colwise
 quantizer -- is documented as "parity unpinned" in ``quant.quant_3d_colwise``.
 """
 
-from . import e4m3, quant, gemm  # noqa: F401
+from . import e4m3, quant, gemm, swiglu  # noqa: F401
