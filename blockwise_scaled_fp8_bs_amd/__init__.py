@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     bs_quant_128x128_both,
     bs_quant_1x128,
     bs_quant_3d_colwise,
+    bs_swiglu_quant_1x128,
     bs_scaled_mm,
     empty_scales,
 )

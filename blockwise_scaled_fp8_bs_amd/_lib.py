@@ -13,6 +13,8 @@ _E = ctypes.c_int  # C enums
 # name -> (restype, argtypes); mirrors include/bs.h
 SIGNATURES = {
     "bs_quant_1x128": (_E, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P]),
+    "bs_swiglu_quant_1x128": (_E, [_P, _P, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
+                                   _P]),
     "bs_quant_128x128": (_E, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P]),
     "bs_quant_3d_colwise": (_E, [_P, _I64, _I64, _I64, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P]),
     "bs_quant_128x128_both": (_E, [_P, _I64, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P, _I64,

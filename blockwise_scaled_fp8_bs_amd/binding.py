@@ -125,6 +125,40 @@ def bs_quant_1x128(x, q_row=None, s_row=None, q_col=None, s_col=None, stream=Non
     _check(_lib.load().bs_quant_1x128(*args, _stream(stream)), "bs_quant_1x128")
 
 
+def bs_swiglu_quant_1x128(a, b, h=None, q_row=None, s_row=None, q_col=None, s_col=None, stream=None):
+    """Gated activation h = silu(a) * b (rounded once to bf16) quantized 1x128
+    along rows and/or transposed columns in one pass; h is written if given.
+
+    a, b [R, C] bf16; h [R, C] bf16 or None; outputs as in bs_quant_1x128.
+    """
+    _mat(a, "a", torch.bfloat16)
+    _mat(b, "b", torch.bfloat16)
+    R, C = a.shape
+    _require(tuple(b.shape) == (R, C), f"b must be [{R}, {C}] like a")
+    args = [_ptr(a), _ptr(b), R, C, _ld(a), _ld(b)]
+    if h is not None:
+        _mat(h, "h", torch.bfloat16)
+        _require(tuple(h.shape) == (R, C), f"h must be [{R}, {C}]")
+        args += [_ptr(h), _ld(h)]
+    else:
+        args += [None, 0]
+    if q_row is not None or s_row is not None:
+        _mat(q_row, "q_row", torch.uint8)
+        _require(tuple(q_row.shape) == (R, C), f"q_row must be [{R}, {C}]")
+        ld_sr = _scale(s_row, "s_row", C // 128, R)
+        args += [_ptr(q_row), _ld(q_row), _ptr(s_row), ld_sr]
+    else:
+        args += [None, 0, None, 0]
+    if q_col is not None or s_col is not None:
+        _mat(q_col, "q_col", torch.uint8)
+        _require(tuple(q_col.shape) == (C, R), f"q_col must be the transpose [{C}, {R}]")
+        ld_sc = _scale(s_col, "s_col", R // 128, C)
+        args += [_ptr(q_col), _ld(q_col), _ptr(s_col), ld_sc]
+    else:
+        args += [None, 0, None, 0]
+    _check(_lib.load().bs_swiglu_quant_1x128(*args, _stream(stream)), "bs_swiglu_quant_1x128")
+
+
 def bs_quant_128x128(x, q, s, stream=None):
     """128x128 quantizer: x [R, C] bf16 -> q [R, C] uint8, s [C/128, >= R/128]."""
     _mat(x, "x", torch.bfloat16)

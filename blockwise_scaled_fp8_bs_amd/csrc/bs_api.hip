@@ -62,13 +62,16 @@ const char* bs_status_string(bs_status st) {
 
 const char* bs_last_error(void) { return g_last_error.c_str(); }
 
-bs_status bs_quant_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x, uint8_t* q_row, int64_t ld_qr,
-                         float* s_row, int64_t ld_sr, uint8_t* q_col, int64_t ld_qc, float* s_col, int64_t ld_sc,
-                         hipStream_t stream) {
-    static const char* fn = "bs_quant_1x128";
+namespace {
+
+// Shared by bs_quant_1x128 and bs_swiglu_quant_1x128 (y, h already checked).
+bs_status quant_1x128_common(const char* fn, const uint16_t* x, const uint16_t* y, int64_t ld_y, uint16_t* h,
+                             int64_t ld_h, int64_t R, int64_t C, int64_t ld_x, uint8_t* q_row, int64_t ld_qr,
+                             float* s_row, int64_t ld_sr, uint8_t* q_col, int64_t ld_qc, float* s_col,
+                             int64_t ld_sc, hipStream_t stream) {
     const bool row = q_row || s_row, col = q_col || s_col;
     const bool empty = R == 0 || C == 0;
-    REQUIRE(x || empty, BS_ERR_NULL, "x is NULL");
+    REQUIRE(x || empty, BS_ERR_NULL, y ? "a is NULL" : "x is NULL");
     REQUIRE(!row || (q_row && s_row) || empty, BS_ERR_NULL, "q_row and s_row must both be set or both NULL");
     REQUIRE(!col || (q_col && s_col) || empty, BS_ERR_NULL, "q_col and s_col must both be set or both NULL");
     REQUIRE(row || col || empty, BS_ERR_NULL, "no output requested (q_row/s_row and q_col/s_col are all NULL)");
@@ -106,8 +109,40 @@ bs_status bs_quant_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x, 
         REQUIRE(aligned16(s_col), BS_ERR_ALIGN, "s_col must be 16-byte aligned");
     }
     if (R == 0 || C == 0) return ok();
-    bs::Quant1x128Args a{x, R, C, ld_x, q_row, ld_qr, s_row, ld_sr, q_col, ld_qc, s_col, ld_sc, C / 128};
-    return hip_status(bs::launch_quant_1x128(a, row, col, stream), fn);
+    bs::Quant1x128Args a{x,    R,     C,     ld_x,  q_row, ld_qr, s_row, ld_sr, q_col, ld_qc,
+                         s_col, ld_sc, C / 128, y,     ld_y,  h,     ld_h};
+    return hip_status(bs::launch_quant_1x128(a, row, col, y != nullptr, stream), fn);
+}
+
+}  // namespace
+
+bs_status bs_quant_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x, uint8_t* q_row, int64_t ld_qr,
+                         float* s_row, int64_t ld_sr, uint8_t* q_col, int64_t ld_qc, float* s_col, int64_t ld_sc,
+                         hipStream_t stream) {
+    return quant_1x128_common("bs_quant_1x128", x, nullptr, 0, nullptr, 0, R, C, ld_x, q_row, ld_qr, s_row, ld_sr,
+                              q_col, ld_qc, s_col, ld_sc, stream);
+}
+
+bs_status bs_swiglu_quant_1x128(const uint16_t* a, const uint16_t* b, int64_t R, int64_t C, int64_t ld_a,
+                                int64_t ld_b, uint16_t* h, int64_t ld_h, uint8_t* q_row, int64_t ld_qr,
+                                float* s_row, int64_t ld_sr, uint8_t* q_col, int64_t ld_qc, float* s_col,
+                                int64_t ld_sc, hipStream_t stream) {
+    static const char* fn = "bs_swiglu_quant_1x128";
+    const bool empty = R == 0 || C == 0;
+    REQUIRE(b || empty, BS_ERR_NULL, "b is NULL");
+    REQUIRE(ld_b >= C, BS_ERR_LAYOUT, "ld_b=%lld < C=%lld: b must be row-major [R, C]", (long long)ld_b,
+            (long long)C);
+    REQUIRE(ld_b < kMaxLd, BS_ERR_LAYOUT, "ld_b=%lld must be < 2^22", (long long)ld_b);
+    REQUIRE(aligned16(b) && ld_b % 8 == 0, BS_ERR_ALIGN, "b must be 16-byte aligned with ld_b %% 8 == 0");
+    if (h) {
+        REQUIRE(ld_h >= C, BS_ERR_LAYOUT, "ld_h=%lld < C=%lld: h is row-major [R, C]", (long long)ld_h,
+                (long long)C);
+        REQUIRE(ld_h < kMaxLd, BS_ERR_LAYOUT, "ld_h=%lld must be < 2^22", (long long)ld_h);
+        REQUIRE(aligned16(h) && ld_h % 8 == 0, BS_ERR_ALIGN, "h must be 16-byte aligned with ld_h %% 8 == 0");
+    }
+    // a takes the place of x in the shared checks
+    return quant_1x128_common(fn, a, empty ? nullptr : b, ld_b, h, ld_h, R, C, ld_a, q_row, ld_qr, s_row, ld_sr,
+                              q_col, ld_qc, s_col, ld_sc, stream);
 }
 
 bs_status bs_quant_128x128(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x, uint8_t* q, int64_t ld_q,

@@ -19,6 +19,12 @@ struct Quant1x128Args {
     float* s_col;
     int64_t ld_sc;
     int64_t col_tiles;  // C / 128
+    // gated form (bs_swiglu_quant_1x128): the quantized tensor is
+    // h = bf16(silu(x) * y), optionally also written to h
+    const uint16_t* y;
+    int64_t ld_y;
+    uint16_t* h;
+    int64_t ld_h;
 };
 
 struct Quant128Args {
@@ -62,7 +68,7 @@ struct GemmArgs {
     int64_t num_tiles;         // grid size (an upper bound for GROUP_M)
 };
 
-hipError_t launch_quant_1x128(const Quant1x128Args& a, bool row, bool col, hipStream_t stream);
+hipError_t launch_quant_1x128(const Quant1x128Args& a, bool row, bool col, bool swiglu, hipStream_t stream);
 hipError_t launch_quant_128x128(const Quant128Args& a, Quant128Mode mode, hipStream_t stream);
 
 // b_1x128: B scales per row (wgrad) instead of per 128x128 block.

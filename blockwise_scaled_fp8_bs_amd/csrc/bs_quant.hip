@@ -108,7 +108,21 @@ __device__ __forceinline__ void col_codes(const TileRegs& tile, const Scale* sc,
     }
 }
 
-template <bool ROW, bool COL>
+// Gated activation of the FFN (silu(a) * b), evaluated in fp32 and rounded
+// once to bf16 (nearest even): the value that gets quantized.
+__device__ __forceinline__ float swiglu_bf16(float a, float b) {
+    const float silu = a / (1.0f + expf(-a));
+    return (float)(__bf16)(silu * b);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+}
+
+// 1x128 quantizer (rows and/or transposed columns).  SWIGLU quantizes
+// h = bf16(silu(x) * y) instead of x, from one read of x and y, and writes
+// h too when a.h is set.
+template <bool ROW, bool COL, bool SWIGLU>
 __global__ __launch_bounds__(kThreads) void quant_1x128_kernel(Quant1x128Args a) {
     __shared__ float s_colmax[2][4][kTile];
     __shared__ __attribute__((aligned(16))) uint8_t s_tr[COL ? 2 : 1][COL ? kTile * kTile : 16];
@@ -121,16 +135,42 @@ __global__ __launch_bounds__(kThreads) void quant_1x128_kernel(Quant1x128Args a)
     int64_t tile = blockIdx.x;
     if (tile >= ntiles) return;
     const int voff_x = (8 * tr) * (int)(a.ld_x * 2) + 16 * tc;
-    Raw raw;
+    const int voff_y = SWIGLU ? (8 * tr) * (int)(a.ld_y * 2) + 16 * tc : 0;
+    Raw raw, raw_y;
     load_raw(a.x, a.ld_x, (tile / a.col_tiles) * kTile, (tile % a.col_tiles) * kTile, a.R, voff_x, raw);
+    if (SWIGLU)
+        load_raw(a.y, a.ld_y, (tile / a.col_tiles) * kTile, (tile % a.col_tiles) * kTile, a.R, voff_y, raw_y);
 
     for (int parity = 0; tile < ntiles; tile += gridDim.x, parity ^= 1) {
         const int64_t r0 = (tile / a.col_tiles) * kTile, c0 = (tile % a.col_tiles) * kTile;
         TileRegs tl;
         unpack_tile(raw, tl);
+        if (SWIGLU) {
+            TileRegs ty;
+            unpack_tile(raw_y, ty);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) tl.f[i][j] = swiglu_bf16(tl.f[i][j], ty.f[i][j]);
+        }
         const int64_t next = tile + gridDim.x;
-        if (next < ntiles)
+        if (next < ntiles) {
             load_raw(a.x, a.ld_x, (next / a.col_tiles) * kTile, (next % a.col_tiles) * kTile, a.R, voff_x, raw);
+            if (SWIGLU)
+                load_raw(a.y, a.ld_y, (next / a.col_tiles) * kTile, (next % a.col_tiles) * kTile, a.R, voff_y,
+                         raw_y);
+        }
+        if (SWIGLU && a.h != nullptr) {
+            const int64_t rows = (a.R - r0) < kTile ? (a.R - r0) : kTile;
+            const __amdgpu_buffer_rsrc_t rh = rsrc(a.h + r0 * a.ld_h + c0, rows * a.ld_h * 2);
+            const int voff_h = (8 * tr) * (int)(a.ld_h * 2) + 16 * tc;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    u32x4{pack_bf16(tl.f[i][0], tl.f[i][1]), pack_bf16(tl.f[i][2], tl.f[i][3]),
+                          pack_bf16(tl.f[i][4], tl.f[i][5]), pack_bf16(tl.f[i][6], tl.f[i][7])},
+                    rh, voff_h, i * (int)(a.ld_h * 2), 0);
+        }
 
         if (ROW) {
             const int64_t rows = (a.R - r0) < kTile ? (a.R - r0) : kTile;
@@ -302,12 +342,17 @@ hipError_t launch_persistent(K kernel, const A& a, int64_t tiles, hipStream_t st
     return hipGetLastError();
 }
 
-hipError_t launch_quant_1x128(const Quant1x128Args& a, bool row, bool col, hipStream_t stream) {
+hipError_t launch_quant_1x128(const Quant1x128Args& a, bool row, bool col, bool swiglu, hipStream_t stream) {
     const int64_t tiles = ((a.R + kTile - 1) / kTile) * a.col_tiles;
     if (tiles == 0) return hipSuccess;
-    if (row && col) return launch_persistent(quant_1x128_kernel<true, true>, a, tiles, stream);
-    if (row) return launch_persistent(quant_1x128_kernel<true, false>, a, tiles, stream);
-    return launch_persistent(quant_1x128_kernel<false, true>, a, tiles, stream);
+    if (swiglu) {
+        if (row && col) return launch_persistent(quant_1x128_kernel<true, true, true>, a, tiles, stream);
+        if (row) return launch_persistent(quant_1x128_kernel<true, false, true>, a, tiles, stream);
+        return launch_persistent(quant_1x128_kernel<false, true, true>, a, tiles, stream);
+    }
+    if (row && col) return launch_persistent(quant_1x128_kernel<true, true, false>, a, tiles, stream);
+    if (row) return launch_persistent(quant_1x128_kernel<true, false, false>, a, tiles, stream);
+    return launch_persistent(quant_1x128_kernel<false, true, false>, a, tiles, stream);
 }
 
 hipError_t launch_quant_128x128(const Quant128Args& a, Quant128Mode mode, hipStream_t stream) {

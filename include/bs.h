@@ -120,6 +120,27 @@ bs_status bs_quant_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x,
                          hipStream_t stream);
 
 /*
+ * bs_swiglu_quant_1x128 -- the gated FFN activation fused with the 1x128
+ * quantizer of its output: h = silu(a) * b (silu(a) = a / (1 + exp(-a)),
+ * evaluated in fp32 and rounded once to bf16, nearest even) is quantized
+ * exactly as bs_quant_1x128 would quantize the bf16 tensor h, from one read
+ * of a and b.  h itself is written only when the h pointer is set.
+ *   a, b   [R, C] bf16 (a = w1 x, b = w2 x of the FFN), ld_a, ld_b >= C
+ *   h      optional [R, C] bf16, ld_h >= C
+ *   q_row/s_row, q_col/s_col  as in bs_quant_1x128 (blocks of h).
+ * h may differ from h computed in float64 and then rounded by one bf16 step
+ * where the exact value lies within fp32 rounding of a tie.
+ * Pages: "add FSDP and TP tests for Float8BlockwiseLinear", summary (the
+ * ToyModel FFN: w1 and w2 feed out_proj); the prototype page, description
+ * (quantization as separate kernels is the overhead to remove).
+ */
+bs_status bs_swiglu_quant_1x128(const uint16_t* a, const uint16_t* b, int64_t R, int64_t C,
+                                int64_t ld_a, int64_t ld_b, uint16_t* h, int64_t ld_h,
+                                uint8_t* q_row, int64_t ld_qr, float* s_row, int64_t ld_sr,
+                                uint8_t* q_col, int64_t ld_qc, float* s_col, int64_t ld_sc,
+                                hipStream_t stream);
+
+/*
  * bs_quant_128x128 -- weight quantizer, one scale per 128x128 tile.
  *   x [R, C] bf16 (R = out features, C = in features = contraction),
  *   q[r * ld_q + c], s[(c / 128) * ld_s + r / 128].

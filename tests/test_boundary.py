@@ -189,3 +189,24 @@ def test_leading_dimensions_are_bounded(lib):
     assert lib.bs_quant_128x128(P, 256, 512, 512, P, big, P, 4, None) == LAYOUT
     assert _q128b(lib, ld_x=big, stride_xg=256 * big) == LAYOUT
     assert _q128b(lib, ld_qt=big, stride_qtg=384 * big) == LAYOUT
+
+
+def _sw(lib, a=P, b=P, R=256, C=512, ld_a=512, ld_b=512, h=None, ld_h=0, q_row=P, ld_qr=512, s_row=P, ld_sr=256,
+        q_col=None, ld_qc=0, s_col=None, ld_sc=0):
+    return lib.bs_swiglu_quant_1x128(a, b, R, C, ld_a, ld_b, h, ld_h, q_row, ld_qr, s_row, ld_sr, q_col, ld_qc,
+                                     s_col, ld_sc, None)
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(b=None), NULL, "b is NULL"),
+    (dict(a=None), NULL, "a is NULL"),
+    (dict(ld_b=256), LAYOUT, "ld_b"),
+    (dict(b=PU), ALIGN, "b must be 16-byte aligned"),
+    (dict(h=P, ld_h=256), LAYOUT, "ld_h"),
+    (dict(h=PU, ld_h=512), ALIGN, "h must be 16-byte aligned"),
+    (dict(C=200, ld_a=200, ld_b=200), SHAPE, "multiple of 128"),
+    (dict(q_row=None, s_row=None), NULL, "no output requested"),
+])
+def test_swiglu_quant_validation(lib, kw, code, frag):
+    assert _sw(lib, **kw) == code
+    assert frag in lib.bs_last_error().decode()
