@@ -47,9 +47,10 @@ def r4(n):
 
 # bench kernel name -> device kernel symbol (as rocprofv3 names it)
 KERNEL_SYMBOL = {
-    "quant_1x128_rowcol(A)": "quant_1x128_kernel<true, true>",
-    "quant_1x128_rowcol(grad_out)": "quant_1x128_kernel<true, true>",
+    "quant_1x128_rowcol(A)": "quant_1x128_kernel<true, true, false>",
+    "quant_1x128_rowcol(grad_out)": "quant_1x128_kernel<true, true, false>",
     "quant_128x128_both(W)": "quant_128x128_kernel<2>",
+    "swiglu_quant": "quant_1x128_kernel<true, true, true>",
     "gemm_fwd": "gemm_kernel<0, false, false>",
     "gemm_dgrad": "gemm_kernel<0, false, false>",
     "gemm_wgrad": "gemm_kernel<0, true, false>",
@@ -366,6 +367,37 @@ def main():
         v.pop("work")
     del src, dst
 
+    # Fusion next to the path: the FFN's gated activation h = silu(a) * b
+    # quantized for the next layer (rows + transposed columns), fused in one
+    # kernel versus torch's silu and mul followed by the quantizer.  a, b are
+    # [M, N] bf16 (here the step's output and grad_out buffers stand in).
+    fa, fb = step.out, step.gout
+    M_, N_ = fa.shape
+
+    def fused():
+        bs.bs_swiglu_quant_1x128(fa, fb, None, step.qg, step.sg, step.qgT, step.sgT)
+
+    def unfused():
+        h = torch.nn.functional.silu(fa) * fb
+        bs.bs_quant_1x128(h, step.qg, step.sg, step.qgT, step.sgT)
+
+    def median_ms(fn, n=7):
+        fn()
+        times = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return sorted(times)[n // 2]
+
+    f_ms, u_ms = median_ms(fused), median_ms(unfused)
+    f_bytes = M_ * N_ * (2 + 2 + 1 + 1) + 4 * (M_ * N_ // 128) * 2
+    fusion = {"shape": [M_, N_], "fused_ms": round(f_ms, 4), "unfused_ms": round(u_ms, 4),
+              "fused_gbs": round(f_bytes / (f_ms * 1e-3) / 1e9, 1), "speedup": round(u_ms / f_ms, 2)}
+
     cpu = None
     if not args.no_cpu_baseline:
         tflops, secs, desc = cpu_oracle_sample(w, rows=min(args.cpu_rows, w.M), seed=args.seed)
@@ -395,6 +427,7 @@ def main():
         "quant_cold_gbs": round(cold_gbs, 1),
         "quant_cold_frac_of_hbm": round(cold_gbs / HBM_PEAK_GBS, 4),
         "quant_cold": cold,
+        "swiglu_quant_fusion": fusion,
         "quant_frac_of_copy": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / copy_gbs, 4),
         "kernels": per_kernel,
         "roofline": roofline,
