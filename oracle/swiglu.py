@@ -13,6 +13,17 @@ Fusing the quantization of h into the kernel that produces it is the first
 fusion next to the blockwise path.  The value quantized is h rounded ONCE to
 bf16 (nearest, ties to even) from its exact value; here h is evaluated in
 float64 (relative error ~1e-16, far below half a bf16 step) and then rounded.
+
+The backward (the derivative of the same function, for the FFN's backward
+pass) quantizes [da | db] for the dgrad and wgrad GEMMs of w1 and w2:
+
+    da = dh * b * silu'(a),  silu'(a) = s (1 + a (1 - s)),  s = 1 / (1 + exp(-a))
+    db = dh * silu(a)
+
+each rounded once to bf16 from its float64 evaluation (1 - s is evaluated as
+1 / (1 + exp(a)) so that no cancellation precedes the one near silu'(a) = 0,
+where a (1 - s) = -1; there the float64 error stays ~1e-14 relative for bf16
+inputs, still far below half a bf16 step).
 """
 
 import numpy as np
@@ -50,3 +61,18 @@ def swiglu(a_bits, b_bits):
     with np.errstate(over="ignore"):
         silu = a / (1.0 + np.exp(-a))          # exp overflow -> inf -> silu = -0
     return round_to_bf16(silu * b)
+
+
+def swiglu_backward(a_bits, b_bits, dh_bits):
+    """(da, db) of h = silu(a) * b for bf16 a, b and upstream gradient dh
+    (uint16 bit patterns), each rounded once to bf16 bits."""
+    a = bf16_bits_to_f32(np.asarray(a_bits, dtype=np.uint16)).astype(np.float64)
+    b = bf16_bits_to_f32(np.asarray(b_bits, dtype=np.uint16)).astype(np.float64)
+    dh = bf16_bits_to_f32(np.asarray(dh_bits, dtype=np.uint16)).astype(np.float64)
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-a))           # sigmoid(a)
+        sn = 1.0 / (1.0 + np.exp(a))           # sigmoid(-a) = 1 - s
+    silu = a * s
+    da = dh * b * s * (1.0 + a * sn)
+    db = dh * silu
+    return round_to_bf16(da), round_to_bf16(db)
