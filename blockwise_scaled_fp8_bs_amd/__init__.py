@@ -20,8 +20,10 @@ from .binding import (  # noqa: F401
     bs_quant_128x128_both,
     bs_quant_1x128,
     bs_quant_3d_colwise,
+    bs_swiglu_bwd_quant_1x128,
     bs_swiglu_quant_1x128,
     bs_scaled_mm,
     empty_scales,
 )
 from .linear import Float8BlockwiseLinear, float8_blockwise_linear, swap_linear_layers  # noqa: F401,E402
+from .ffn import Float8BlockwiseGatedFFN, float8_blockwise_gated_ffn  # noqa: F401,E402

@@ -15,6 +15,8 @@ SIGNATURES = {
     "bs_quant_1x128": (_E, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P]),
     "bs_swiglu_quant_1x128": (_E, [_P, _P, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
                                    _P]),
+    "bs_swiglu_bwd_quant_1x128": (_E, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P,
+                                       _I64, _P, _I64, _P]),
     "bs_quant_128x128": (_E, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P]),
     "bs_quant_3d_colwise": (_E, [_P, _I64, _I64, _I64, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P]),
     "bs_quant_128x128_both": (_E, [_P, _I64, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P, _I64,

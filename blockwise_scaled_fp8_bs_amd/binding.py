@@ -159,6 +159,42 @@ def bs_swiglu_quant_1x128(a, b, h=None, q_row=None, s_row=None, q_col=None, s_co
     _check(_lib.load().bs_swiglu_quant_1x128(*args, _stream(stream)), "bs_swiglu_quant_1x128")
 
 
+def bs_swiglu_bwd_quant_1x128(a, b, dh, dab=None, q_row=None, s_row=None, q_col=None, s_col=None, stream=None):
+    """Backward of h = silu(a) * b fused with the 1x128 quantizer: quantizes
+    the [R, 2C] matrix [da | db] (da = dh b silu'(a), db = dh silu(a), each
+    rounded once to bf16) along rows and/or transposed columns.
+
+    a, b, dh [R, C] bf16; dab [R, 2C] bf16 or None; q_row [R, 2C] uint8 with
+    s_row [2C/128, >= R]; q_col [2C, R] uint8 with s_col [R/128, >= 2C].
+    """
+    for t, name in ((a, "a"), (b, "b"), (dh, "dh")):
+        _mat(t, name, torch.bfloat16)
+    R, C = a.shape
+    _require(tuple(b.shape) == (R, C) and tuple(dh.shape) == (R, C), f"b and dh must be [{R}, {C}] like a")
+    args = [_ptr(a), _ptr(b), _ptr(dh), R, C, _ld(a), _ld(b), _ld(dh)]
+    if dab is not None:
+        _mat(dab, "dab", torch.bfloat16)
+        _require(tuple(dab.shape) == (R, 2 * C), f"dab must be [{R}, {2 * C}]")
+        args += [_ptr(dab), _ld(dab)]
+    else:
+        args += [None, 0]
+    if q_row is not None or s_row is not None:
+        _mat(q_row, "q_row", torch.uint8)
+        _require(tuple(q_row.shape) == (R, 2 * C), f"q_row must be [{R}, {2 * C}]")
+        ld_sr = _scale(s_row, "s_row", 2 * C // 128, R)
+        args += [_ptr(q_row), _ld(q_row), _ptr(s_row), ld_sr]
+    else:
+        args += [None, 0, None, 0]
+    if q_col is not None or s_col is not None:
+        _mat(q_col, "q_col", torch.uint8)
+        _require(tuple(q_col.shape) == (2 * C, R), f"q_col must be the transpose [{2 * C}, {R}]")
+        ld_sc = _scale(s_col, "s_col", R // 128, 2 * C)
+        args += [_ptr(q_col), _ld(q_col), _ptr(s_col), ld_sc]
+    else:
+        args += [None, 0, None, 0]
+    _check(_lib.load().bs_swiglu_bwd_quant_1x128(*args, _stream(stream)), "bs_swiglu_bwd_quant_1x128")
+
+
 def bs_quant_128x128(x, q, s, stream=None):
     """128x128 quantizer: x [R, C] bf16 -> q [R, C] uint8, s [C/128, >= R/128]."""
     _mat(x, "x", torch.bfloat16)

@@ -145,6 +145,61 @@ bs_status bs_swiglu_quant_1x128(const uint16_t* a, const uint16_t* b, int64_t R,
                               q_col, ld_qc, s_col, ld_sc, stream);
 }
 
+bs_status bs_swiglu_bwd_quant_1x128(const uint16_t* a, const uint16_t* b, const uint16_t* dh, int64_t R,
+                                    int64_t C, int64_t ld_a, int64_t ld_b, int64_t ld_dh, uint16_t* dab,
+                                    int64_t ld_dab, uint8_t* q_row, int64_t ld_qr, float* s_row, int64_t ld_sr,
+                                    uint8_t* q_col, int64_t ld_qc, float* s_col, int64_t ld_sc,
+                                    hipStream_t stream) {
+    static const char* fn = "bs_swiglu_bwd_quant_1x128";
+    const bool row = q_row || s_row, col = q_col || s_col;
+    const bool empty = R == 0 || C == 0;
+    REQUIRE((a && b && dh) || empty, BS_ERR_NULL, "a, b and dh must be non-NULL");
+    REQUIRE(!row || (q_row && s_row) || empty, BS_ERR_NULL, "q_row and s_row must both be set or both NULL");
+    REQUIRE(!col || (q_col && s_col) || empty, BS_ERR_NULL, "q_col and s_col must both be set or both NULL");
+    REQUIRE(row || col || empty, BS_ERR_NULL, "no output requested (q_row/s_row and q_col/s_col are all NULL)");
+    REQUIRE(R >= 0 && C >= 0, BS_ERR_SHAPE, "R=%lld C=%lld must be >= 0", (long long)R, (long long)C);
+    REQUIRE(C % 128 == 0, BS_ERR_SHAPE, "C=%lld must be a multiple of 128 (1x128 blocks along rows)",
+            (long long)C);
+    REQUIRE(!col || R % 128 == 0, BS_ERR_SHAPE,
+            "R=%lld must be a multiple of 128 for the column output (128-row blocks)", (long long)R);
+    const struct { const uint16_t* p; int64_t ld; const char* name; } ins[3] = {{a, ld_a, "a"}, {b, ld_b, "b"},
+                                                                             {dh, ld_dh, "dh"}};
+    for (const auto& in : ins) {
+        REQUIRE(in.ld >= C && in.ld < kMaxLd, BS_ERR_LAYOUT, "ld of %s = %lld must be >= C=%lld and < 2^22",
+                in.name, (long long)in.ld, (long long)C);
+        REQUIRE(aligned16(in.p) && in.ld % 8 == 0, BS_ERR_ALIGN, "%s must be 16-byte aligned with ld %% 8 == 0",
+                in.name);
+    }
+    if (dab) {
+        REQUIRE(ld_dab >= 2 * C && ld_dab < kMaxLd, BS_ERR_LAYOUT, "ld_dab=%lld must be >= 2C=%lld and < 2^22",
+                (long long)ld_dab, (long long)(2 * C));
+        REQUIRE(aligned16(dab) && ld_dab % 8 == 0, BS_ERR_ALIGN, "dab must be 16-byte aligned with ld_dab %% 8 == 0");
+    }
+    if (row) {
+        REQUIRE(ld_qr >= 2 * C && ld_qr < kMaxLd, BS_ERR_LAYOUT,
+                "ld_qr=%lld must be >= 2C=%lld (q_row is [R, 2C]) and < 2^22", (long long)ld_qr, (long long)(2 * C));
+        REQUIRE(ld_sr >= R && ld_sr % 4 == 0, BS_ERR_LAYOUT,
+                "ld_sr=%lld must be >= R=%lld and a multiple of 4 (s_row is K-major [2C/128][ld_sr])",
+                (long long)ld_sr, (long long)R);
+        REQUIRE(aligned16(q_row) && ld_qr % 16 == 0 && aligned16(s_row), BS_ERR_ALIGN,
+                "q_row and s_row must be 16-byte aligned with ld_qr %% 16 == 0");
+    }
+    if (col) {
+        REQUIRE(ld_qc >= R && ld_qc < kMaxLd, BS_ERR_LAYOUT,
+                "ld_qc=%lld must be >= R=%lld (q_col is the transpose [2C, R]) and < 2^22", (long long)ld_qc,
+                (long long)R);
+        REQUIRE(ld_sc >= 2 * C && ld_sc % 4 == 0, BS_ERR_LAYOUT,
+                "ld_sc=%lld must be >= 2C=%lld and a multiple of 4 (s_col is K-major [R/128][ld_sc])",
+                (long long)ld_sc, (long long)(2 * C));
+        REQUIRE(aligned16(q_col) && ld_qc % 16 == 0 && aligned16(s_col), BS_ERR_ALIGN,
+                "q_col and s_col must be 16-byte aligned with ld_qc %% 16 == 0");
+    }
+    if (empty) return ok();
+    bs::SwigluBwdArgs args{a,     b,     dh,    R,     C,     ld_a,  ld_b,  ld_dh, dab,   ld_dab,
+                           q_row, ld_qr, s_row, ld_sr, q_col, ld_qc, s_col, ld_sc, C / 128};
+    return hip_status(bs::launch_swiglu_bwd_quant(args, row, col, stream), fn);
+}
+
 bs_status bs_quant_128x128(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x, uint8_t* q, int64_t ld_q,
                            float* s, int64_t ld_s, hipStream_t stream) {
     static const char* fn = "bs_quant_128x128";

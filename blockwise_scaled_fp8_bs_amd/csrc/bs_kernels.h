@@ -27,6 +27,24 @@ struct Quant1x128Args {
     int64_t ld_h;
 };
 
+// Backward of the gated activation fused with the 1x128 quantizer: inputs
+// a, b, dh are [R, C]; the quantized matrix is [da | db], [R, 2C].
+struct SwigluBwdArgs {
+    const uint16_t *a, *b, *dh;
+    int64_t R, C, ld_a, ld_b, ld_dh;
+    uint16_t* dab;  // optional [R, 2C] bf16 output of [da | db]
+    int64_t ld_dab;
+    uint8_t* q_row;  // [R, 2C]
+    int64_t ld_qr;
+    float* s_row;    // [2C/128][ld_sr >= R]
+    int64_t ld_sr;
+    uint8_t* q_col;  // [2C, R]
+    int64_t ld_qc;
+    float* s_col;    // [R/128][ld_sc >= 2C]
+    int64_t ld_sc;
+    int64_t col_tiles;  // C / 128
+};
+
 struct Quant128Args {
     const uint16_t* x;
     int64_t G, R, C, stride_xg, ld_x;
@@ -70,6 +88,7 @@ struct GemmArgs {
 
 hipError_t launch_quant_1x128(const Quant1x128Args& a, bool row, bool col, bool swiglu, hipStream_t stream);
 hipError_t launch_quant_128x128(const Quant128Args& a, Quant128Mode mode, hipStream_t stream);
+hipError_t launch_swiglu_bwd_quant(const SwigluBwdArgs& a, bool row, bool col, hipStream_t stream);
 
 // b_1x128: B scales per row (wgrad) instead of per 128x128 block.
 hipError_t launch_gemm(const GemmArgs& a, GroupKind kind, bool b_1x128, bool out_f32, hipStream_t stream);

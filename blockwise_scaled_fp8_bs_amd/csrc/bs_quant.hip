@@ -108,15 +108,180 @@ __device__ __forceinline__ void col_codes(const TileRegs& tile, const Scale* sc,
     }
 }
 
-// Gated activation of the FFN (silu(a) * b), evaluated in fp32 and rounded
-// once to bf16 (nearest even): the value that gets quantized.
+// ---- the FFN's gated activation h = silu(a) * b and its derivative ----
+// The value quantized is the float64 formula rounded once to bf16 (nearest
+// even).  Each kernel evaluates it in fp32 (relative error below 2^-20 where
+// no intermediate leaves the normal range) and takes that value's bf16
+// rounding unless it lies within the error bound of a rounding tie, where
+// (rarely) the float64 formula is evaluated instead.
+
+// Distance of r from the nearest bf16 rounding tie, in fp32 units in the last
+// place (the low 16 bits of r against the half step 0x8000).
+__device__ __forceinline__ float tie_distance(float r) {
+    const uint32_t low = __float_as_uint(r) & 0xFFFFu;
+    return (float)(low >= 0x8000u ? low - 0x8000u : 0x8000u - low);
+}
+
+// float64 -> bf16 (as float), nearest even, one rounding: the fp64 -> fp32
+// step rounds to odd (truncate, set the last bit if inexact), which keeps 16
+// more bits than bf16, so the final fp32 -> bf16 rounding is the correct one.
+__device__ __forceinline__ float bf16_from_double(double d) {
+    float f = (float)d;
+    if ((double)f != d) {
+        uint32_t u = __float_as_uint(f);
+        if (fabs((double)f) > fabs(d)) u -= 1u;  // step toward zero (inf -> FLT_MAX)
+        f = __uint_as_float(u | 1u);
+    }
+    return (float)(__bf16)f;
+}
+
+constexpr float kTieWindow = 32.0f;   // fp32 ulps; the fp32 paths err by < 6
+constexpr float kMinNormal = 1.17549435e-38f;  // 2^-126
+
+// The float64 evaluations, out of line: they run for a few elements in a
+// thousand, and one copy keeps the unrolled fp32 paths small.
+__device__ __attribute__((noinline)) float swiglu_bf16_f64(float a, float b) {
+    const double ad = a;
+    return bf16_from_double(ad / (1.0 + exp(-ad)) * (double)b);
+}
+
+__device__ __attribute__((noinline)) float2 swiglu_grad_bf16_f64(float a, float b, float dh) {
+    const double ad = a, bd = b, dd = dh;
+    const double sd = 1.0 / (1.0 + exp(-ad));
+    const double snd = 1.0 / (1.0 + exp(ad));
+    return make_float2(bf16_from_double(dd * bd * sd * (1.0 + ad * snd)), bf16_from_double(dd * (ad * sd)));
+}
+
+// h = silu(a) * b rounded once to bf16.  fp32 unless a <= -69 (exp(-a) near
+// fp32 overflow), silu(a) subnormal, or the value near a tie.
 __device__ __forceinline__ float swiglu_bf16(float a, float b) {
-    const float silu = a / (1.0f + expf(-a));
-    return (float)(__bf16)(silu * b);
+    if (a > -69.0f) {
+        const float silu = a / (1.0f + expf(-a));
+        const float r = silu * b;
+        const bool normal = silu == 0.0f || fabsf(silu) >= kMinNormal;
+        if (normal && __builtin_isfinite(r) && tie_distance(r) > kTieWindow) return (float)(__bf16)r;
+    }
+    return swiglu_bf16_f64(a, b);
+}
+
+// da = dh * b * silu'(a) and db = dh * silu(a), silu'(a) = s (1 + a (1 - s)),
+// s = 1 / (1 + exp(-a)), each rounded once to bf16.  1 - s is taken as
+// 1 / (1 + exp(a)); near silu'(a) = 0 the sum 1 + a (1 - s) cancels, so its
+// tie window grows with |a (1 - s)| / |1 + a (1 - s)| (infinite at 0).
+__device__ __forceinline__ void swiglu_grad_bf16(float a, float b, float dh, float& da, float& db) {
+    if (a > -69.0f) {
+        const float s = 1.0f / (1.0f + expf(-a));
+        const float sn = 1.0f / (1.0f + expf(a));
+        const float t = __builtin_fmaf(a, sn, 1.0f);
+        const float p1 = dh * b, p2 = p1 * s;
+        const float rda = p2 * t;
+        const float silu = a * s;
+        const float rdb = dh * silu;
+        const bool ok_a = __builtin_isfinite(rda) &&
+                          (p1 == 0.0f || (fabsf(p1) >= kMinNormal && fabsf(p2) >= kMinNormal)) &&
+                          tie_distance(rda) > kTieWindow + 8.0f * fabsf(a * sn) / fabsf(t);
+        const bool ok_b = __builtin_isfinite(rdb) && (silu == 0.0f || fabsf(silu) >= kMinNormal) &&
+                          tie_distance(rdb) > kTieWindow;
+        if (ok_a && ok_b) {
+            da = (float)(__bf16)rda;
+            db = (float)(__bf16)rdb;
+            return;
+        }
+    }
+    const float2 g = swiglu_grad_bf16_f64(a, b, dh);
+    da = g.x;
+    db = g.y;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+}
+
+// 1x128 row blocks of one tile: codes to q (the tile's first element; rows
+// past `rows` are dropped), scales to s (the tile's entries of one K-major
+// scale row).
+__device__ __forceinline__ void quant_tile_rows(const TileRegs& tl, int64_t rows, uint8_t* q, int64_t ld_q,
+                                                float* s, int tr, int tc) {
+    const __amdgpu_buffer_rsrc_t rq = rsrc(q, rows * ld_q);
+    const int voff_q = (8 * tr) * (int)ld_q + 8 * tc;
+    float my_scale = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float m = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(tl.f[i][j]));
+        const uint32_t amax_bits = row16_max(__float_as_uint(m));
+        const Scale sc = block_scale(__uint_as_float(amax_bits));
+        const uint2 qv = quant8(tl.f[i], sc);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{qv.x, qv.y}, rq, voff_q, i * (int)ld_q, 0);
+        if ((tc & 7) == i) my_scale = sc.s;
+    }
+    // lanes tc < 8 store the scale of row 8*tr + tc: 32 consecutive rows per wave
+    const __amdgpu_buffer_rsrc_t rs = rsrc(s, rows * 4);
+    if (tc < 8) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(my_scale), rs, (8 * tr + tc) * 4, 0, 0);
+}
+
+// 1x128 column blocks (the tile's 128 rows) of one tile: codes written
+// transposed to qt (row c0 of q^T, column r0), scales to s (128 consecutive
+// entries of one K-major scale row).  colmax and tr_lds are this call's LDS
+// buffers (alternate between consecutive calls); it holds barriers, so every
+// thread of the workgroup calls it.
+__device__ __forceinline__ void quant_tile_cols(const TileRegs& tl, uint8_t* qt, int64_t ld_qt, float* s,
+                                                float (*colmax)[kTile], uint8_t* tr_lds, int tr, int tc, int wave) {
+    float cm[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float m = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(tl.f[i][j]));
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        cm[j] = m;
+    }
+    if ((threadIdx.x & 63) < 16) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) colmax[wave][8 * tc + j] = cm[j];
+    }
+    __syncthreads();
+    Scale sc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int c = 8 * tc + j;
+        const float m = fmaxf(fmaxf(colmax[0][c], colmax[1][c]), fmaxf(colmax[2][c], colmax[3][c]));
+        sc[j] = block_scale(m);
+    }
+    uint2 codes[8];
+    col_codes(tl, sc, codes);
+    if (threadIdx.x < 16) {
+        const __amdgpu_buffer_rsrc_t rs = rsrc(s, kTile * 4);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{__float_as_uint(sc[0].s), __float_as_uint(sc[1].s), __float_as_uint(sc[2].s),
+                  __float_as_uint(sc[3].s)}, rs, 32 * tc, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{__float_as_uint(sc[4].s), __float_as_uint(sc[5].s), __float_as_uint(sc[6].s),
+                  __float_as_uint(sc[7].s)}, rs, 32 * tc + 16, 0, 0);
+    }
+    store_transposed(tr_lds, codes, tr, tc, qt, ld_qt);
+}
+
+// bf16 values of a tile's rows (already bf16-exact floats) -> packed rows.
+__device__ __forceinline__ void pack_tile(const TileRegs& tl, Raw& raw) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        raw.v[i] = make_uint4(pack_bf16(tl.f[i][0], tl.f[i][1]), pack_bf16(tl.f[i][2], tl.f[i][3]),
+                              pack_bf16(tl.f[i][4], tl.f[i][5]), pack_bf16(tl.f[i][6], tl.f[i][7]));
+}
+
+// Packed rows of a tile to out (the tile's first element; rows past `rows`
+// are dropped).
+__device__ __forceinline__ void store_raw(const Raw& raw, uint16_t* out, int64_t ld_out, int64_t rows, int tr,
+                                          int tc) {
+    const __amdgpu_buffer_rsrc_t ro = rsrc(out, rows * ld_out * 2);
+    const int voff = (8 * tr) * (int)(ld_out * 2) + 16 * tc;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{raw.v[i].x, raw.v[i].y, raw.v[i].z, raw.v[i].w}, ro, voff,
+                                               i * (int)(ld_out * 2), 0);
 }
 
 // 1x128 quantizer (rows and/or transposed columns).  SWIGLU quantizes
@@ -143,6 +308,7 @@ __global__ __launch_bounds__(kThreads) void quant_1x128_kernel(Quant1x128Args a)
 
     for (int parity = 0; tile < ntiles; tile += gridDim.x, parity ^= 1) {
         const int64_t r0 = (tile / a.col_tiles) * kTile, c0 = (tile % a.col_tiles) * kTile;
+        const int64_t rows = (a.R - r0) < kTile ? (a.R - r0) : kTile;
         TileRegs tl;
         unpack_tile(raw, tl);
         if (SWIGLU) {
@@ -161,75 +327,84 @@ __global__ __launch_bounds__(kThreads) void quant_1x128_kernel(Quant1x128Args a)
                          raw_y);
         }
         if (SWIGLU && a.h != nullptr) {
-            const int64_t rows = (a.R - r0) < kTile ? (a.R - r0) : kTile;
-            const __amdgpu_buffer_rsrc_t rh = rsrc(a.h + r0 * a.ld_h + c0, rows * a.ld_h * 2);
-            const int voff_h = (8 * tr) * (int)(a.ld_h * 2) + 16 * tc;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    u32x4{pack_bf16(tl.f[i][0], tl.f[i][1]), pack_bf16(tl.f[i][2], tl.f[i][3]),
-                          pack_bf16(tl.f[i][4], tl.f[i][5]), pack_bf16(tl.f[i][6], tl.f[i][7])},
-                    rh, voff_h, i * (int)(a.ld_h * 2), 0);
+            Raw ph;
+            pack_tile(tl, ph);
+            store_raw(ph, a.h + r0 * a.ld_h + c0, a.ld_h, rows, tr, tc);
         }
+        if (ROW) quant_tile_rows(tl, rows, a.q_row + r0 * a.ld_qr + c0, a.ld_qr, a.s_row + (c0 / kTile) * a.ld_sr + r0, tr, tc);
+        if (COL)
+            quant_tile_cols(tl, a.q_col + c0 * a.ld_qc + r0, a.ld_qc, a.s_col + (r0 / kTile) * a.ld_sc + c0,
+                            s_colmax[parity], s_tr[parity], tr, tc, wave);
+    }
+}
 
-        if (ROW) {
-            const int64_t rows = (a.R - r0) < kTile ? (a.R - r0) : kTile;
-            const __amdgpu_buffer_rsrc_t rq = rsrc(a.q_row + r0 * a.ld_qr + c0, rows * a.ld_qr);
-            const int voff_q = (8 * tr) * (int)a.ld_qr + 8 * tc;
-            float my_scale = 0.f;
+// Backward of the gated activation fused with the 1x128 quantizer: from one
+// read of a, b and dh ([R, C] bf16) it forms da and db (each rounded once to
+// bf16) and quantizes the [R, 2C] matrix [da | db] along rows and/or its
+// transposed columns; [da | db] itself is written when a.dab is set.  Each
+// input tile gives two output tiles: da's at columns c0, db's at C + c0.
+template <bool ROW, bool COL>
+__global__ __launch_bounds__(kThreads) void swiglu_bwd_quant_kernel(SwigluBwdArgs a) {
+    __shared__ float s_colmax[2][4][kTile];
+    __shared__ __attribute__((aligned(16))) uint8_t s_tr[COL ? 2 : 1][COL ? kTile * kTile : 16];
+
+    const int t = threadIdx.x;
+    const int tr = t >> 4, tc = t & 15;
+    const int wave = t >> 6;
+    const int64_t ntiles = ((a.R + kTile - 1) / kTile) * a.col_tiles;
+
+    int64_t tile = blockIdx.x;
+    if (tile >= ntiles) return;
+    const int voff_a = (8 * tr) * (int)(a.ld_a * 2) + 16 * tc;
+    const int voff_b = (8 * tr) * (int)(a.ld_b * 2) + 16 * tc;
+    const int voff_d = (8 * tr) * (int)(a.ld_dh * 2) + 16 * tc;
+    auto load3 = [&](int64_t tl_id, Raw& ra, Raw& rb, Raw& rd) {
+        const int64_t r0 = (tl_id / a.col_tiles) * kTile, c0 = (tl_id % a.col_tiles) * kTile;
+        load_raw(a.a, a.ld_a, r0, c0, a.R, voff_a, ra);
+        load_raw(a.b, a.ld_b, r0, c0, a.R, voff_b, rb);
+        load_raw(a.dh, a.ld_dh, r0, c0, a.R, voff_d, rd);
+    };
+    Raw ra, rb, rd;
+    load3(tile, ra, rb, rd);
+
+    int parity = 0;
+    for (; tile < ntiles; tile += gridDim.x) {
+        const int64_t r0 = (tile / a.col_tiles) * kTile, c0 = (tile % a.col_tiles) * kTile;
+        const int64_t rows = (a.R - r0) < kTile ? (a.R - r0) : kTile;
+        const int64_t C = a.col_tiles * kTile;
+        Raw pda, pdb;  // da and db of the tile, packed bf16
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float m = 0.f;
+        for (int i = 0; i < 8; ++i) {
+            float fa[8], fb[8], fd[8], ga[8], gb[8];
+            unpack8(ra.v[i], fa);
+            unpack8(rb.v[i], fb);
+            unpack8(rd.v[i], fd);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(tl.f[i][j]));
-                const uint32_t amax_bits = row16_max(__float_as_uint(m));
-                const Scale sc = block_scale(__uint_as_float(amax_bits));
-                const uint2 q = quant8(tl.f[i], sc);
-                __builtin_amdgcn_raw_buffer_store_b64(u32x2{q.x, q.y}, rq, voff_q, i * (int)a.ld_qr, 0);
-                if ((tc & 7) == i) my_scale = sc.s;
-            }
-            // lanes tc < 8 store the scale of row 8*tr + tc: 32 consecutive rows per wave
-            const __amdgpu_buffer_rsrc_t rs = rsrc(a.s_row + (c0 / kTile) * a.ld_sr + r0, rows * 4);
-            if (tc < 8) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(my_scale), rs, (8 * tr + tc) * 4, 0, 0);
+            for (int j = 0; j < 8; ++j) swiglu_grad_bf16(fa[j], fb[j], fd[j], ga[j], gb[j]);
+            pda.v[i] = make_uint4(pack_bf16(ga[0], ga[1]), pack_bf16(ga[2], ga[3]), pack_bf16(ga[4], ga[5]),
+                                  pack_bf16(ga[6], ga[7]));
+            pdb.v[i] = make_uint4(pack_bf16(gb[0], gb[1]), pack_bf16(gb[2], gb[3]), pack_bf16(gb[4], gb[5]),
+                                  pack_bf16(gb[6], gb[7]));
         }
-
-        if (COL) {
-            // column amax over the tile's 128 rows
-            float cm[8];
+        const int64_t next = tile + gridDim.x;
+        if (next < ntiles) load3(next, ra, rb, rd);
+        if (a.dab != nullptr) {
+            store_raw(pda, a.dab + r0 * a.ld_dab + c0, a.ld_dab, rows, tr, tc);
+            store_raw(pdb, a.dab + r0 * a.ld_dab + C + c0, a.ld_dab, rows, tr, tc);
+        }
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                float m = 0.f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(tl.f[i][j]));
-                m = fmaxf(m, __shfl_xor(m, 16));
-                m = fmaxf(m, __shfl_xor(m, 32));
-                cm[j] = m;
+        for (int half = 0; half < 2; ++half) {
+            const int64_t co = (half ? C : 0) + c0;  // output column of the tile
+            TileRegs tl;
+            unpack_tile(half ? pdb : pda, tl);
+            if (ROW)
+                quant_tile_rows(tl, rows, a.q_row + r0 * a.ld_qr + co, a.ld_qr, a.s_row + (co / kTile) * a.ld_sr + r0,
+                                tr, tc);
+            if (COL) {
+                quant_tile_cols(tl, a.q_col + co * a.ld_qc + r0, a.ld_qc, a.s_col + (r0 / kTile) * a.ld_sc + co,
+                                s_colmax[parity], s_tr[parity], tr, tc, wave);
+                parity ^= 1;
             }
-            if ((t & 63) < 16) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) s_colmax[parity][wave][8 * tc + j] = cm[j];
-            }
-            __syncthreads();
-            Scale sc[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int c = 8 * tc + j;
-                const float m = fmaxf(fmaxf(s_colmax[parity][0][c], s_colmax[parity][1][c]),
-                                      fmaxf(s_colmax[parity][2][c], s_colmax[parity][3][c]));
-                sc[j] = block_scale(m);
-            }
-            uint2 codes[8];
-            col_codes(tl, sc, codes);
-            if (t < 16) {
-                const __amdgpu_buffer_rsrc_t rs = rsrc(a.s_col + (r0 / kTile) * a.ld_sc + c0, kTile * 4);
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    u32x4{__float_as_uint(sc[0].s), __float_as_uint(sc[1].s), __float_as_uint(sc[2].s),
-                          __float_as_uint(sc[3].s)}, rs, 32 * tc, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    u32x4{__float_as_uint(sc[4].s), __float_as_uint(sc[5].s), __float_as_uint(sc[6].s),
-                          __float_as_uint(sc[7].s)}, rs, 32 * tc + 16, 0, 0);
-            }
-            store_transposed(s_tr[parity], codes, tr, tc, a.q_col + c0 * a.ld_qc + r0, a.ld_qc);
         }
     }
 }
@@ -353,6 +528,14 @@ hipError_t launch_quant_1x128(const Quant1x128Args& a, bool row, bool col, bool 
     if (row && col) return launch_persistent(quant_1x128_kernel<true, true, false>, a, tiles, stream);
     if (row) return launch_persistent(quant_1x128_kernel<true, false, false>, a, tiles, stream);
     return launch_persistent(quant_1x128_kernel<false, true, false>, a, tiles, stream);
+}
+
+hipError_t launch_swiglu_bwd_quant(const SwigluBwdArgs& a, bool row, bool col, hipStream_t stream) {
+    const int64_t tiles = ((a.R + kTile - 1) / kTile) * a.col_tiles;
+    if (tiles == 0) return hipSuccess;
+    if (row && col) return launch_persistent(swiglu_bwd_quant_kernel<true, true>, a, tiles, stream);
+    if (row) return launch_persistent(swiglu_bwd_quant_kernel<true, false>, a, tiles, stream);
+    return launch_persistent(swiglu_bwd_quant_kernel<false, true>, a, tiles, stream);
 }
 
 hipError_t launch_quant_128x128(const Quant128Args& a, Quant128Mode mode, hipStream_t stream) {

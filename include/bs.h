@@ -121,15 +121,15 @@ bs_status bs_quant_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x,
 
 /*
  * bs_swiglu_quant_1x128 -- the gated FFN activation fused with the 1x128
- * quantizer of its output: h = silu(a) * b (silu(a) = a / (1 + exp(-a)),
- * evaluated in fp32 and rounded once to bf16, nearest even) is quantized
- * exactly as bs_quant_1x128 would quantize the bf16 tensor h, from one read
- * of a and b.  h itself is written only when the h pointer is set.
+ * quantizer of its output: h = silu(a) * b (silu(a) = a / (1 + exp(-a)); the
+ * value of this formula in float64, rounded once to bf16, nearest even) is
+ * quantized exactly as bs_quant_1x128 would quantize the bf16 tensor h, from
+ * one read of a and b.  h itself is written only when the h pointer is set.
  *   a, b   [R, C] bf16 (a = w1 x, b = w2 x of the FFN), ld_a, ld_b >= C
  *   h      optional [R, C] bf16, ld_h >= C
  *   q_row/s_row, q_col/s_col  as in bs_quant_1x128 (blocks of h).
- * h may differ from h computed in float64 and then rounded by one bf16 step
- * where the exact value lies within fp32 rounding of a tie.
+ * The kernel evaluates in fp32 and switches to float64 for the rare values
+ * whose fp32 result lies within its error bound of a bf16 rounding tie.
  * Pages: "add FSDP and TP tests for Float8BlockwiseLinear", summary (the
  * ToyModel FFN: w1 and w2 feed out_proj); the prototype page, description
  * (quantization as separate kernels is the overhead to remove).
@@ -139,6 +139,34 @@ bs_status bs_swiglu_quant_1x128(const uint16_t* a, const uint16_t* b, int64_t R,
                                 uint8_t* q_row, int64_t ld_qr, float* s_row, int64_t ld_sr,
                                 uint8_t* q_col, int64_t ld_qc, float* s_col, int64_t ld_sc,
                                 hipStream_t stream);
+
+/*
+ * bs_swiglu_bwd_quant_1x128 -- the backward of the same activation fused with
+ * the 1x128 quantizer of its result: from one read of a, b and the upstream
+ * gradient dh it forms
+ *   da = dh * b * silu'(a),  silu'(a) = s (1 + a (1 - s)),  s = 1 / (1 + exp(-a))
+ *   db = dh * silu(a)
+ * (each the float64 value of its formula, 1 - s evaluated as
+ * 1 / (1 + exp(a)), rounded once to bf16) and quantizes the [R, 2C] matrix
+ * [da | db] -- da in columns [0, C), db in [C, 2C) -- exactly as
+ * bs_quant_1x128 would: its rows feed the dgrad GEMM of the stacked
+ * [w1; w2] weight, its transposed columns that weight's wgrad GEMM.
+ *   a, b, dh  [R, C] bf16, ld_a, ld_b, ld_dh >= C
+ *   dab       optional [R, 2C] bf16 output of [da | db], ld_dab >= 2C
+ *   q_row, s_row   both NULL or both set: [R, 2C] codes, ld_qr >= 2C;
+ *                  s_row[(c / 128) * ld_sr + r], ld_sr >= R
+ *   q_col, s_col   both NULL or both set: [2C, R] codes, ld_qc >= R;
+ *                  s_col[(r / 128) * ld_sc + c], ld_sc >= 2C
+ *   C % 128 == 0; R % 128 == 0 when the col output is requested.
+ * Errors as bs_quant_1x128.
+ * Pages: "add FSDP and TP tests for Float8BlockwiseLinear", summary (the
+ * ToyModel FFN and its backward); the prototype page, description.
+ */
+bs_status bs_swiglu_bwd_quant_1x128(const uint16_t* a, const uint16_t* b, const uint16_t* dh, int64_t R,
+                                    int64_t C, int64_t ld_a, int64_t ld_b, int64_t ld_dh, uint16_t* dab,
+                                    int64_t ld_dab, uint8_t* q_row, int64_t ld_qr, float* s_row, int64_t ld_sr,
+                                    uint8_t* q_col, int64_t ld_qc, float* s_col, int64_t ld_sc,
+                                    hipStream_t stream);
 
 /*
  * bs_quant_128x128 -- weight quantizer, one scale per 128x128 tile.

@@ -210,3 +210,31 @@ def _sw(lib, a=P, b=P, R=256, C=512, ld_a=512, ld_b=512, h=None, ld_h=0, q_row=P
 def test_swiglu_quant_validation(lib, kw, code, frag):
     assert _sw(lib, **kw) == code
     assert frag in lib.bs_last_error().decode()
+
+
+def _swb(lib, a=P, b=P, dh=P, R=256, C=512, ld_a=512, ld_b=512, ld_dh=512, dab=None, ld_dab=0, q_row=P,
+         ld_qr=1024, s_row=P, ld_sr=256, q_col=P, ld_qc=256, s_col=P, ld_sc=1024):
+    return lib.bs_swiglu_bwd_quant_1x128(a, b, dh, R, C, ld_a, ld_b, ld_dh, dab, ld_dab, q_row, ld_qr, s_row, ld_sr,
+                                         q_col, ld_qc, s_col, ld_sc, None)
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(dh=None), NULL, "a, b and dh"),
+    (dict(ld_dh=256), LAYOUT, "ld of dh"),
+    (dict(b=PU), ALIGN, "b must be 16-byte aligned"),
+    (dict(dab=P, ld_dab=512), LAYOUT, "ld_dab"),
+    (dict(ld_qr=512), LAYOUT, "ld_qr"),
+    (dict(ld_sc=512), LAYOUT, "ld_sc"),
+    (dict(ld_sr=255), LAYOUT, "ld_sr"),
+    (dict(R=200), SHAPE, "multiple of 128 for the column output"),
+    (dict(C=200, ld_a=200, ld_b=200, ld_dh=200), SHAPE, "multiple of 128"),
+    (dict(q_row=None, s_row=None, q_col=None, s_col=None), NULL, "no output requested"),
+    (dict(s_col=None), NULL, "q_col and s_col"),
+])
+def test_swiglu_bwd_quant_validation(lib, kw, code, frag):
+    assert _swb(lib, **kw) == code
+    assert frag in lib.bs_last_error().decode()
+
+
+def test_swiglu_bwd_quant_empty_is_ok(lib):
+    assert _swb(lib, R=0, a=None, b=None, dh=None) == OK

@@ -1,9 +1,11 @@
-"""Host-side checks of the Float8BlockwiseLinear wrapper (no GPU needed):
-argument validation happens before any kernel call, with clear messages."""
+"""Host-side checks of the Float8BlockwiseLinear wrapper and the gated FFN
+module (no GPU needed): argument validation happens before any kernel call,
+with clear messages."""
 
 import pytest
 import torch
 
+import blockwise_scaled_fp8_bs_amd as bs
 from blockwise_scaled_fp8_bs_amd import Float8BlockwiseLinear, float8_blockwise_linear, swap_linear_layers
 
 
@@ -40,3 +42,45 @@ def test_swap_replaces_bias_free_linears_only():
     assert torch.equal(m[0].weight, ref[0].to(torch.bfloat16)) and torch.equal(m[2][0].weight, ref[1].to(torch.bfloat16))
     with pytest.raises(ValueError, match="bias"):
         Float8BlockwiseLinear.from_linear(torch.nn.Linear(128, 128))
+
+
+# ---- the gated FFN module: argument checks (no GPU needed) ----
+
+def _ffn_args(M=256, D=256, H=512, dtype=torch.bfloat16):
+    x = torch.zeros((M, D), dtype=dtype)
+    return x, torch.zeros((H, D), dtype=dtype), torch.zeros((H, D), dtype=dtype), torch.zeros((D, H), dtype=dtype)
+
+
+def test_gated_ffn_rejects_bad_arguments():
+    x, w1, w2, wo = _ffn_args()
+    with pytest.raises(ValueError, match="bfloat16"):
+        bs.float8_blockwise_gated_ffn(x.float(), w1, w2, wo)
+    with pytest.raises(ValueError, match="contiguous"):
+        bs.float8_blockwise_gated_ffn(x.t(), w1, w2, wo)
+    with pytest.raises(ValueError, match="w1 and w2"):
+        bs.float8_blockwise_gated_ffn(x, w1, w2[:384], wo)
+    with pytest.raises(ValueError, match="out_proj must be"):
+        bs.float8_blockwise_gated_ffn(x, w1, w2, wo[:, :384].contiguous())
+    with pytest.raises(ValueError, match="features"):
+        bs.float8_blockwise_gated_ffn(torch.zeros((256, 384), dtype=torch.bfloat16), w1, w2, wo)
+    x6, a6, b6, o6 = _ffn_args(H=640)
+    with pytest.raises(ValueError, match="multiple of 512"):
+        bs.float8_blockwise_gated_ffn(x6, a6, b6, o6)
+    x1, a1, b1, o1 = _ffn_args(M=200)
+    with pytest.raises(ValueError, match="multiple of 128"):
+        bs.float8_blockwise_gated_ffn(x1, a1, b1, o1)
+    with pytest.raises(ValueError, match="GPU"):
+        bs.float8_blockwise_gated_ffn(x, w1, w2, wo)
+
+
+def test_gated_ffn_module_shapes_and_conversion():
+    with pytest.raises(ValueError, match="multiple of 512"):
+        bs.Float8BlockwiseGatedFFN(256, 640)
+    lin = [torch.nn.Linear(256, 512, bias=False), torch.nn.Linear(256, 512, bias=False),
+           torch.nn.Linear(512, 256, bias=False)]
+    m = bs.Float8BlockwiseGatedFFN.from_linears(*lin)
+    assert (m.dim, m.hidden) == (256, 512)
+    assert m.w1.dtype == torch.bfloat16 and tuple(m.out_proj.shape) == (256, 512)
+    assert torch.equal(m.w2, lin[1].weight.detach().to(torch.bfloat16))
+    with pytest.raises(ValueError, match="biases"):
+        bs.Float8BlockwiseGatedFFN.from_linears(torch.nn.Linear(256, 512), lin[1], lin[2])

@@ -69,3 +69,38 @@ class OracleLinear(torch.nn.Module):
         K = self.weight.shape[1]
         y = _OracleLinearFn.apply(x.reshape(-1, K), self.weight)
         return y.view(*x.shape[:-1], self.weight.shape[0])
+
+
+class _OracleSwiGLUFn(torch.autograd.Function):
+    """h = silu(a) * b rounded once to bf16 by the oracle; backward in float64
+    (da = dh b silu'(a), db = dh silu(a)), rounded to bf16."""
+
+    @staticmethod
+    def forward(ctx, a, b):
+        from oracle import swiglu as oswiglu
+        ctx.save_for_backward(a, b)
+        h = oswiglu.swiglu(_bits(a), _bits(b))
+        return torch.from_numpy(h.view(np.int16).copy()).view(torch.bfloat16).view(a.shape)
+
+    @staticmethod
+    def backward(ctx, dh):
+        a, b = ctx.saved_tensors
+        a64, b64, dh64 = a.double(), b.double(), dh.double()
+        sig = torch.sigmoid(a64)
+        da = dh64 * b64 * sig * (1.0 + a64 * (1.0 - sig))
+        db = dh64 * a64 * sig
+        return da.to(torch.bfloat16), db.to(torch.bfloat16)
+
+
+class OracleGatedFFN(torch.nn.Module):
+    """The gated FFN with oracle-recipe layers and the oracle's once-rounded
+    gated activation: the reference of the fused gated FFN module."""
+
+    def __init__(self, dim, hidden):
+        super().__init__()
+        self.w1 = OracleLinear(dim, hidden)
+        self.w2 = OracleLinear(dim, hidden)
+        self.out_proj = OracleLinear(hidden, dim)
+
+    def forward(self, x):
+        return self.out_proj(_OracleSwiGLUFn.apply(self.w1(x), self.w2(x)))
