@@ -221,6 +221,41 @@ def blas_threads():
     return os.cpu_count()
 
 
+def ffn_module_timing(M, D, H, median_ms, seed):
+    """Median fwd+bwd time of the fused gated FFN module and of the same FFN
+    built from three Float8BlockwiseLinear layers (same weights and input)."""
+    fused = bs.Float8BlockwiseGatedFFN(D, H, device="cuda")
+    lin = [bs.Float8BlockwiseLinear(D, H, device="cuda"), bs.Float8BlockwiseLinear(D, H, device="cuda"),
+           bs.Float8BlockwiseLinear(H, D, device="cuda")]
+    with torch.no_grad():
+        for k, name in enumerate(["w1", "w2", "out_proj"]):
+            wt = inputs.bf16_normal(tuple(getattr(fused, name).shape), 0.02, seed + 10 + k).cuda()
+            getattr(fused, name).copy_(wt)
+            lin[k].weight.copy_(wt)
+    x = inputs.bf16_normal((M, D), 1.0, seed + 20).cuda().requires_grad_()
+    dy = inputs.bf16_normal((M, D), 0.01, seed + 21).cuda()
+    params = [fused.w1, fused.w2, fused.out_proj] + [l.weight for l in lin]
+
+    def clear():
+        x.grad = None
+        for p_ in params:
+            p_.grad = None
+
+    def run_fused():
+        clear()
+        fused(x).backward(dy)
+
+    def run_unfused():
+        clear()
+        lin[2](torch.nn.functional.silu(lin[0](x)) * lin[1](x)).backward(dy)
+
+    f_ms, u_ms = median_ms(run_fused, 5), median_ms(run_unfused, 5)
+    flops = 2.0 * M * D * H * 3 * 3
+    return {"shape": {"tokens": M, "dim": D, "hidden": H}, "fused_ms": round(f_ms, 4),
+            "unfused_ms": round(u_ms, 4), "speedup": round(u_ms / f_ms, 3),
+            "fused_tflops": round(flops / (f_ms * 1e-3) / 1e12, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -229,6 +264,7 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(inputs.WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ffn-module", action="store_true", help="skip the gated FFN module timing")
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="tokens of the workload the CPU oracle baseline runs on (capped at M)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -398,6 +434,41 @@ def main():
     fusion = {"shape": [M_, N_], "fused_ms": round(f_ms, 4), "unfused_ms": round(u_ms, 4),
               "fused_gbs": round(f_bytes / (f_ms * 1e-3) / 1e9, 1), "speedup": round(u_ms / f_ms, 2)}
 
+    # ... and its backward: [da | db] from a, b, dh quantized (rows + columns
+    # of the [M, 2N] matrix) in one kernel, versus the same float32
+    # arithmetic in torch followed by the quantizer.
+    fd = inputs.bf16_normal((M_, N_), 0.01, args.seed + 30).cuda()
+    qd = torch.empty((M_, 2 * N_), dtype=torch.uint8, device="cuda")
+    sd = bs.empty_scales(2 * N_ // 128, M_, "cuda")
+    qdt = torch.empty((2 * N_, M_), dtype=torch.uint8, device="cuda")
+    sdt = bs.empty_scales(M_ // 128, 2 * N_, "cuda")
+    dab = torch.empty((M_, 2 * N_), dtype=torch.bfloat16, device="cuda")
+
+    def fused_bwd():
+        bs.bs_swiglu_bwd_quant_1x128(fa, fb, fd, None, qd, sd, qdt, sdt)
+
+    def unfused_bwd():
+        a32, b32, d32 = fa.float(), fb.float(), fd.float()
+        sig = torch.sigmoid(a32)
+        dab[:, :N_] = d32 * b32 * sig * (1.0 + a32 * (1.0 - sig))
+        dab[:, N_:] = d32 * a32 * sig
+        bs.bs_quant_1x128(dab, qd, sd, qdt, sdt)
+
+    fb_ms, ub_ms = median_ms(fused_bwd), median_ms(unfused_bwd)
+    fb_bytes = M_ * N_ * (3 * 2 + 4 * 1) + 4 * (2 * M_ * N_ // 128) * 2
+    fusion_bwd = {"shape": [M_, N_], "fused_ms": round(fb_ms, 4), "unfused_ms": round(ub_ms, 4),
+                  "fused_gbs": round(fb_bytes / (fb_ms * 1e-3) / 1e9, 1), "speedup": round(ub_ms / fb_ms, 2)}
+    del qd, qdt, dab, fd
+
+    # The gated FFN out_proj(silu(w1 x) * w2 x) as one module (shared input
+    # quantization, stacked w1/w2 GEMMs, the fused activation quantizer)
+    # against three Float8BlockwiseLinear layers with torch's silu and mul:
+    # one forward + backward each, dim = K and hidden = N of the workload.
+    ffn = None
+    if w.G == 1 and w.N % 512 == 0 and not args.no_ffn_module:
+        ffn = ffn_module_timing(w.M, w.K, w.N, median_ms, args.seed)
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         tflops, secs, desc = cpu_oracle_sample(w, rows=min(args.cpu_rows, w.M), seed=args.seed)
@@ -428,6 +499,8 @@ def main():
         "quant_cold_frac_of_hbm": round(cold_gbs / HBM_PEAK_GBS, 4),
         "quant_cold": cold,
         "swiglu_quant_fusion": fusion,
+        "swiglu_bwd_quant_fusion": fusion_bwd,
+        "gated_ffn_module": ffn,
         "quant_frac_of_copy": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / copy_gbs, 4),
         "kernels": per_kernel,
         "roofline": roofline,

@@ -135,7 +135,7 @@ __device__ __forceinline__ float bf16_from_double(double d) {
     return (float)(__bf16)f;
 }
 
-constexpr float kTieWindow = 32.0f;   // fp32 ulps; the fp32 paths err by < 6
+constexpr float kTieWindow = 16.0f;   // fp32 ulps; the fp32 paths err by < 6
 constexpr float kMinNormal = 1.17549435e-38f;  // 2^-126
 
 // The float64 evaluations, out of line: they run for a few elements in a
@@ -145,7 +145,8 @@ __device__ __attribute__((noinline)) float swiglu_bf16_f64(float a, float b) {
     return bf16_from_double(ad / (1.0 + exp(-ad)) * (double)b);
 }
 
-__device__ __attribute__((noinline)) float2 swiglu_grad_bf16_f64(float a, float b, float dh) {
+// da and db in float64 for the elements the fp32 path leaves undecided.
+__device__ __forceinline__ float2 swiglu_grad_bf16_f64(float a, float b, float dh) {
     const double ad = a, bd = b, dd = dh;
     const double sd = 1.0 / (1.0 + exp(-ad));
     const double snd = 1.0 / (1.0 + exp(ad));
@@ -164,37 +165,83 @@ __device__ __forceinline__ float swiglu_bf16(float a, float b) {
     return swiglu_bf16_f64(a, b);
 }
 
+// Undecided elements of the gradient come out with da = +inf (bf16 0x7F80),
+// which marks them for the float64 pass (a true +inf is just recomputed).
+constexpr uint32_t kRedoBits = 0x7F80u;
+
 // da = dh * b * silu'(a) and db = dh * silu(a), silu'(a) = s (1 + a (1 - s)),
-// s = 1 / (1 + exp(-a)), each rounded once to bf16.  1 - s is taken as
-// 1 / (1 + exp(a)); near silu'(a) = 0 the sum 1 + a (1 - s) cancels, so its
-// tie window grows with |a (1 - s)| / |1 + a (1 - s)| (infinite at 0).
-__device__ __forceinline__ void swiglu_grad_bf16(float a, float b, float dh, float& da, float& db) {
-    if (a > -69.0f) {
-        const float s = 1.0f / (1.0f + expf(-a));
-        const float sn = 1.0f / (1.0f + expf(a));
-        const float t = __builtin_fmaf(a, sn, 1.0f);
-        const float p1 = dh * b, p2 = p1 * s;
-        const float rda = p2 * t;
-        const float silu = a * s;
-        const float rdb = dh * silu;
-        const bool ok_a = __builtin_isfinite(rda) &&
-                          (p1 == 0.0f || (fabsf(p1) >= kMinNormal && fabsf(p2) >= kMinNormal)) &&
-                          tie_distance(rda) > kTieWindow + 8.0f * fabsf(a * sn) / fabsf(t);
-        const bool ok_b = __builtin_isfinite(rdb) && (silu == 0.0f || fabsf(silu) >= kMinNormal) &&
-                          tie_distance(rdb) > kTieWindow;
-        if (ok_a && ok_b) {
-            da = (float)(__bf16)rda;
-            db = (float)(__bf16)rdb;
-            return;
-        }
-    }
-    const float2 g = swiglu_grad_bf16_f64(a, b, dh);
-    da = g.x;
-    db = g.y;
+// s = 1 / (1 + exp(-a)), in fp32, each rounded to bf16; da = +inf where
+// either rounding is not certain to be the float64 formula's (a <= -69,
+// an intermediate outside the normal range, or a value near a tie).  1 - s is
+// taken as 1 / (1 + exp(a)); near silu'(a) = 0 the sum t = 1 + a (1 - s)
+// cancels, so da's window adds 8 |a (1 - s)| / |t| ulps (infinite at t = 0),
+// written without a division.
+__device__ __forceinline__ void swiglu_grad_fast(float a, float b, float dh, float& da, float& db) {
+    const float s = 1.0f / (1.0f + expf(-a));
+    const float sn = 1.0f / (1.0f + expf(a));
+    const float t = __builtin_fmaf(a, sn, 1.0f);
+    const float p1 = dh * b, p2 = p1 * s;
+    const float rda = p2 * t;
+    const float silu = a * s;
+    const float rdb = dh * silu;
+    const bool ok_a = __builtin_isfinite(rda) && (p1 == 0.0f || (fabsf(p1) >= kMinNormal && fabsf(p2) >= kMinNormal)) &&
+                      (tie_distance(rda) - kTieWindow) * fabsf(t) > 8.0f * fabsf(a * sn);
+    const bool ok_b = __builtin_isfinite(rdb) && (silu == 0.0f || fabsf(silu) >= kMinNormal) &&
+                      tie_distance(rdb) > kTieWindow;
+    const bool ok = a > -69.0f && ok_a && ok_b;
+    da = ok ? (float)(__bf16)rda : __builtin_inff();
+    db = (float)(__bf16)rdb;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+}
+
+// Word k (0..31, static) of a thread's packed 8x8 block: row k / 4,
+// columns 2 (k % 4) and 2 (k % 4) + 1.
+__device__ __forceinline__ uint32_t raw_word(const Raw& r, int k) {
+    const uint4 v = r.v[k >> 2];
+    return (k & 3) == 0 ? v.x : (k & 3) == 1 ? v.y : (k & 3) == 2 ? v.z : v.w;
+}
+
+// Replaces element e (per lane: row e / 8, column e % 8) of a packed block by
+// a bf16-exact value: selects over the 32 words (rare path).
+__device__ __forceinline__ void raw_set(Raw& r, int e, float v) {
+    const int w = e >> 1;
+    const uint32_t h16 = __float_as_uint(v) >> 16;
+    const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+    const uint32_t put = (e & 1) ? (h16 << 16) : h16;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (4 * i + 0 == w) r.v[i].x = (r.v[i].x & keep) | put;
+        if (4 * i + 1 == w) r.v[i].y = (r.v[i].y & keep) | put;
+        if (4 * i + 2 == w) r.v[i].z = (r.v[i].z & keep) | put;
+        if (4 * i + 3 == w) r.v[i].w = (r.v[i].w & keep) | put;
+    }
+}
+
+// Re-evaluates, in float64, the elements of a thread's packed block that the
+// fp32 path marked (+inf); fn(e) does element e.  The marks are found with
+// integer arithmetic only (per-element compares would keep 64 lane masks
+// alive), and the loop runs per lane: a wave spends one pass per marked
+// element of its busiest lane (usually none or one per tile).
+template <typename F>
+__device__ __forceinline__ void fixup_block(const Raw& marked, F&& fn) {
+    uint32_t m[2] = {0u, 0u};  // elements 0..31, 32..63
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+        const uint32_t w = raw_word(marked, k);
+        const uint32_t lo = ((w & 0xFFFFu) ^ kRedoBits) - 1u, hi = ((w >> 16) ^ kRedoBits) - 1u;
+        m[k >> 4] |= ((lo >> 31) << ((2 * k) & 31)) | ((hi >> 31) << ((2 * k + 1) & 31));
+    }
+    for (int h = 0; h < 2; ++h) {
+        uint32_t mask = m[h];
+        while (mask != 0) {
+            const int e = 32 * h + __builtin_ctz(mask);
+            mask &= mask - 1;
+            fn(e);
+        }
+    }
 }
 
 // 1x128 row blocks of one tile: codes to q (the tile's first element; rows
@@ -364,15 +411,16 @@ __global__ __launch_bounds__(kThreads) void swiglu_bwd_quant_kernel(SwigluBwdArg
         load_raw(a.b, a.ld_b, r0, c0, a.R, voff_b, rb);
         load_raw(a.dh, a.ld_dh, r0, c0, a.R, voff_d, rd);
     };
-    Raw ra, rb, rd;
-    load3(tile, ra, rb, rd);
-
     int parity = 0;
     for (; tile < ntiles; tile += gridDim.x) {
         const int64_t r0 = (tile / a.col_tiles) * kTile, c0 = (tile % a.col_tiles) * kTile;
         const int64_t rows = (a.R - r0) < kTile ? (a.R - r0) : kTile;
         const int64_t C = a.col_tiles * kTile;
-        Raw pda, pdb;  // da and db of the tile, packed bf16
+        // No prefetch of the next tile: a, b and dh of two tiles would not fit
+        // beside the outputs; two workgroups per SIMD hide the latency instead.
+        Raw ra, rb, rd;
+        load3(tile, ra, rb, rd);
+        Raw pda, pdb;  // da and db of the tile, packed bf16 (da marked where undecided)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             float fa[8], fb[8], fd[8], ga[8], gb[8];
@@ -380,14 +428,22 @@ __global__ __launch_bounds__(kThreads) void swiglu_bwd_quant_kernel(SwigluBwdArg
             unpack8(rb.v[i], fb);
             unpack8(rd.v[i], fd);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) swiglu_grad_bf16(fa[j], fb[j], fd[j], ga[j], gb[j]);
+            for (int j = 0; j < 8; ++j) swiglu_grad_fast(fa[j], fb[j], fd[j], ga[j], gb[j]);
             pda.v[i] = make_uint4(pack_bf16(ga[0], ga[1]), pack_bf16(ga[2], ga[3]), pack_bf16(ga[4], ga[5]),
                                   pack_bf16(ga[6], ga[7]));
             pdb.v[i] = make_uint4(pack_bf16(gb[0], gb[1]), pack_bf16(gb[2], gb[3]), pack_bf16(gb[4], gb[5]),
                                   pack_bf16(gb[6], gb[7]));
         }
-        const int64_t next = tile + gridDim.x;
-        if (next < ntiles) load3(next, ra, rb, rd);
+        // undecided elements: their inputs are read again (a few per tile)
+        fixup_block(pda, [&](int e) {
+            const int64_t r = r0 + 8 * tr + (e >> 3), c = c0 + 8 * tc + (e & 7);
+            if (r >= a.R) return;  // rows past the end read as zeros and are never marked
+            const float2 g = swiglu_grad_bf16_f64(__uint_as_float((uint32_t)a.a[r * a.ld_a + c] << 16),
+                                                  __uint_as_float((uint32_t)a.b[r * a.ld_b + c] << 16),
+                                                  __uint_as_float((uint32_t)a.dh[r * a.ld_dh + c] << 16));
+            raw_set(pda, e, g.x);
+            raw_set(pdb, e, g.y);
+        });
         if (a.dab != nullptr) {
             store_raw(pda, a.dab + r0 * a.ld_dab + c0, a.ld_dab, rows, tr, tc);
             store_raw(pdb, a.dab + r0 * a.ld_dab + C + c0, a.ld_dab, rows, tr, tc);
