@@ -65,6 +65,7 @@ KERNEL_SYMBOL = {
 KERNEL_SOURCES = {
     "gemm_kernel": ["bs_gemm.hip", "bs_kernels.h"],
     "quant_": ["bs_quant.hip", "bs_device.h", "bs_kernels.h"],
+    "swiglu_bwd_quant_kernel": ["bs_quant.hip", "bs_device.h", "bs_kernels.h"],
 }
 
 
@@ -265,6 +266,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ffn-module", action="store_true", help="skip the gated FFN module timing")
+    ap.add_argument("--no-fusion", action="store_true",
+                    help="skip the fused gated-activation timings (keeps per-kernel profiles to the step's shapes)")
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="tokens of the workload the CPU oracle baseline runs on (capped at M)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -409,13 +412,7 @@ def main():
     # [M, N] bf16 (here the step's output and grad_out buffers stand in).
     fa, fb = step.out, step.gout
     M_, N_ = fa.shape
-
-    def fused():
-        bs.bs_swiglu_quant_1x128(fa, fb, None, step.qg, step.sg, step.qgT, step.sgT)
-
-    def unfused():
-        h = torch.nn.functional.silu(fa) * fb
-        bs.bs_quant_1x128(h, step.qg, step.sg, step.qgT, step.sgT)
+    fusion = fusion_bwd = None
 
     def median_ms(fn, n=7):
         fn()
@@ -429,36 +426,44 @@ def main():
             times.append(e0.elapsed_time(e1))
         return sorted(times)[n // 2]
 
-    f_ms, u_ms = median_ms(fused), median_ms(unfused)
-    f_bytes = M_ * N_ * (2 + 2 + 1 + 1) + 4 * (M_ * N_ // 128) * 2
-    fusion = {"shape": [M_, N_], "fused_ms": round(f_ms, 4), "unfused_ms": round(u_ms, 4),
-              "fused_gbs": round(f_bytes / (f_ms * 1e-3) / 1e9, 1), "speedup": round(u_ms / f_ms, 2)}
+    if not args.no_fusion:
+        def fused():
+            bs.bs_swiglu_quant_1x128(fa, fb, None, step.qg, step.sg, step.qgT, step.sgT)
 
-    # ... and its backward: [da | db] from a, b, dh quantized (rows + columns
-    # of the [M, 2N] matrix) in one kernel, versus the same float32
-    # arithmetic in torch followed by the quantizer.
-    fd = inputs.bf16_normal((M_, N_), 0.01, args.seed + 30).cuda()
-    qd = torch.empty((M_, 2 * N_), dtype=torch.uint8, device="cuda")
-    sd = bs.empty_scales(2 * N_ // 128, M_, "cuda")
-    qdt = torch.empty((2 * N_, M_), dtype=torch.uint8, device="cuda")
-    sdt = bs.empty_scales(M_ // 128, 2 * N_, "cuda")
-    dab = torch.empty((M_, 2 * N_), dtype=torch.bfloat16, device="cuda")
+        def unfused():
+            h = torch.nn.functional.silu(fa) * fb
+            bs.bs_quant_1x128(h, step.qg, step.sg, step.qgT, step.sgT)
 
-    def fused_bwd():
-        bs.bs_swiglu_bwd_quant_1x128(fa, fb, fd, None, qd, sd, qdt, sdt)
+        f_ms, u_ms = median_ms(fused), median_ms(unfused)
+        f_bytes = M_ * N_ * (2 + 2 + 1 + 1) + 4 * (M_ * N_ // 128) * 2
+        fusion = {"shape": [M_, N_], "fused_ms": round(f_ms, 4), "unfused_ms": round(u_ms, 4),
+                  "fused_gbs": round(f_bytes / (f_ms * 1e-3) / 1e9, 1), "speedup": round(u_ms / f_ms, 2)}
 
-    def unfused_bwd():
-        a32, b32, d32 = fa.float(), fb.float(), fd.float()
-        sig = torch.sigmoid(a32)
-        dab[:, :N_] = d32 * b32 * sig * (1.0 + a32 * (1.0 - sig))
-        dab[:, N_:] = d32 * a32 * sig
-        bs.bs_quant_1x128(dab, qd, sd, qdt, sdt)
+        # ... and its backward: [da | db] from a, b, dh quantized (rows + columns
+        # of the [M, 2N] matrix) in one kernel, versus the same float32
+        # arithmetic in torch followed by the quantizer.
+        fd = inputs.bf16_normal((M_, N_), 0.01, args.seed + 30).cuda()
+        qd = torch.empty((M_, 2 * N_), dtype=torch.uint8, device="cuda")
+        sd = bs.empty_scales(2 * N_ // 128, M_, "cuda")
+        qdt = torch.empty((2 * N_, M_), dtype=torch.uint8, device="cuda")
+        sdt = bs.empty_scales(M_ // 128, 2 * N_, "cuda")
+        dab = torch.empty((M_, 2 * N_), dtype=torch.bfloat16, device="cuda")
 
-    fb_ms, ub_ms = median_ms(fused_bwd), median_ms(unfused_bwd)
-    fb_bytes = M_ * N_ * (3 * 2 + 4 * 1) + 4 * (2 * M_ * N_ // 128) * 2
-    fusion_bwd = {"shape": [M_, N_], "fused_ms": round(fb_ms, 4), "unfused_ms": round(ub_ms, 4),
-                  "fused_gbs": round(fb_bytes / (fb_ms * 1e-3) / 1e9, 1), "speedup": round(ub_ms / fb_ms, 2)}
-    del qd, qdt, dab, fd
+        def fused_bwd():
+            bs.bs_swiglu_bwd_quant_1x128(fa, fb, fd, None, qd, sd, qdt, sdt)
+
+        def unfused_bwd():
+            a32, b32, d32 = fa.float(), fb.float(), fd.float()
+            sig = torch.sigmoid(a32)
+            dab[:, :N_] = d32 * b32 * sig * (1.0 + a32 * (1.0 - sig))
+            dab[:, N_:] = d32 * a32 * sig
+            bs.bs_quant_1x128(dab, qd, sd, qdt, sdt)
+
+        fb_ms, ub_ms = median_ms(fused_bwd), median_ms(unfused_bwd)
+        fb_bytes = M_ * N_ * (3 * 2 + 4 * 1) + 4 * (2 * M_ * N_ // 128) * 2
+        fusion_bwd = {"shape": [M_, N_], "fused_ms": round(fb_ms, 4), "unfused_ms": round(ub_ms, 4),
+                      "fused_gbs": round(fb_bytes / (fb_ms * 1e-3) / 1e9, 1), "speedup": round(ub_ms / fb_ms, 2)}
+        del qd, qdt, dab, fd
 
     # The gated FFN out_proj(silu(w1 x) * w2 x) as one module (shared input
     # quantization, stacked w1/w2 GEMMs, the fused activation quantizer)
