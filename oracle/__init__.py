@@ -17,8 +17,11 @@ What it computes (plain numpy, slow on purpose):
 * ``gemm``   -- the blockwise-scaled matmuls as "dequantize to float64, then
   float64 matmul", dense and grouped, plus the per-element tolerance of the
   parity bar.
-* ``swiglu`` -- the gated FFN activation silu(a) * b rounded once to bf16
-  (what the fused activation-and-quantize kernel quantizes).
+* ``swiglu`` -- the gated FFN activation silu(a) * b and its derivative,
+  each rounded once to bf16 (what the fused activation-and-quantize kernels
+  quantize).
+* ``mx``     -- the MXFP8 variant (OCP Microscaling: 32-element blocks, E8M0
+  power-of-two scales, E4M3 elements) quantizer and its GEMM.
 
 Sources: the three pytorch/ao pull-request pages on blockwise FP8 training
 ("[not for land] float8 blockwise scaling training prototype using
