@@ -16,6 +16,8 @@ from .binding import (  # noqa: F401
     bs_diag_division,
     bs_diag_e4m3_census,
     bs_grouped_scaled_mm,
+    bs_mx_quant_1x32,
+    bs_mx_scaled_mm,
     bs_quant_128x128,
     bs_quant_128x128_both,
     bs_quant_1x128,
@@ -23,6 +25,7 @@ from .binding import (  # noqa: F401
     bs_swiglu_bwd_quant_1x128,
     bs_swiglu_quant_1x128,
     bs_scaled_mm,
+    empty_mx_scales,
     empty_scales,
 )
 from .linear import Float8BlockwiseLinear, float8_blockwise_linear, swap_linear_layers  # noqa: F401,E402

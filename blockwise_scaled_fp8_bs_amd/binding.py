@@ -195,6 +195,65 @@ def bs_swiglu_bwd_quant_1x128(a, b, dh, dab=None, q_row=None, s_row=None, q_col=
     _check(_lib.load().bs_swiglu_bwd_quant_1x128(*args, _stream(stream)), "bs_swiglu_bwd_quant_1x128")
 
 
+def empty_mx_scales(nchunks, count, device, pad=0):
+    """Allocate a K-major MX scale tensor [nchunks, roundup16(count) + pad] of E8M0 bytes (uint8)."""
+    return torch.empty((nchunks, (count + 15) // 16 * 16 + pad), dtype=torch.uint8, device=device)
+
+
+def _mx_scale(t, name, nch, count):
+    _mat(t, name, torch.uint8)
+    _require(t.shape[0] == nch, f"{name} must have {nch} rows (one per 32-block of the contraction), got {t.shape[0]}")
+    _require(t.shape[1] >= count, f"{name} must have at least {count} columns (K-major [K/32][>= {count}] bytes)")
+    return t.stride(0)
+
+
+def bs_mx_quant_1x32(x, q_row=None, s_row=None, q_col=None, s_col=None, stream=None):
+    """MXFP8 quantizer (32-element blocks, E8M0 scale bytes), rows and/or
+    transposed columns in one pass.
+
+    x [R, C] bf16; q_row [R, C] uint8 with s_row [C/32, >= R] uint8;
+    q_col [C, R] uint8 with s_col [R/32, >= C] uint8.
+    """
+    _mat(x, "x", torch.bfloat16)
+    R, C = x.shape
+    args = [_ptr(x), R, C, _ld(x)]
+    if q_row is not None or s_row is not None:
+        _mat(q_row, "q_row", torch.uint8)
+        _require(tuple(q_row.shape) == (R, C), f"q_row must be [{R}, {C}]")
+        args += [_ptr(q_row), _ld(q_row), _ptr(s_row), _mx_scale(s_row, "s_row", C // 32, R)]
+    else:
+        args += [None, 0, None, 0]
+    if q_col is not None or s_col is not None:
+        _mat(q_col, "q_col", torch.uint8)
+        _require(tuple(q_col.shape) == (C, R), f"q_col must be the transpose [{C}, {R}]")
+        args += [_ptr(q_col), _ld(q_col), _ptr(s_col), _mx_scale(s_col, "s_col", R // 32, C)]
+    else:
+        args += [None, 0, None, 0]
+    _check(_lib.load().bs_mx_quant_1x32(*args, _stream(stream)), "bs_mx_quant_1x32")
+
+
+def bs_mx_scaled_mm(a, sa, b, sb, out=None, out_dtype=torch.bfloat16, stream=None):
+    """D[M, N] = A [M, K] . B [N, K]^T with MX (E8M0, 32-element) scales
+    sa [K/32, >= M] and sb [K/32, >= N] (uint8).  Returns ``out``."""
+    _mat(a, "a", torch.uint8)
+    _mat(b, "b", torch.uint8)
+    M, K = a.shape
+    N, Kb = b.shape
+    _require(K == Kb, f"a is [M, {K}] but b is [N, {Kb}]: both must be contiguous along the same K")
+    ld_sa = _mx_scale(sa, "sa", K // 32, M)
+    ld_sb = _mx_scale(sb, "sb", K // 32, N)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _mat(out, "out", out.dtype)
+    _require(tuple(out.shape) == (M, N), f"out must be [{M}, {N}]")
+    dt = {torch.bfloat16: BS_OUT_BF16, torch.float32: BS_OUT_F32}.get(out.dtype)
+    _require(dt is not None, "out must be bfloat16 or float32")
+    _check(_lib.load().bs_mx_scaled_mm(M, N, K, _ptr(a), _ld(a), _ptr(sa), ld_sa, _ptr(b), _ld(b), _ptr(sb), ld_sb,
+                                       _ptr(out), _ld(out), dt, _stream(stream)),
+           "bs_mx_scaled_mm")
+    return out
+
+
 def bs_quant_128x128(x, q, s, stream=None):
     """128x128 quantizer: x [R, C] bf16 -> q [R, C] uint8, s [C/128, >= R/128]."""
     _mat(x, "x", torch.bfloat16)

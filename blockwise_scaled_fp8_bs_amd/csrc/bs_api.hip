@@ -6,6 +6,7 @@
 
 #include "../../include/bs.h"
 #include "bs_kernels.h"
+#include "bs_mx.h"
 
 namespace {
 
@@ -198,6 +199,88 @@ bs_status bs_swiglu_bwd_quant_1x128(const uint16_t* a, const uint16_t* b, const 
     bs::SwigluBwdArgs args{a,     b,     dh,    R,     C,     ld_a,  ld_b,  ld_dh, dab,   ld_dab,
                            q_row, ld_qr, s_row, ld_sr, q_col, ld_qc, s_col, ld_sc, C / 128};
     return hip_status(bs::launch_swiglu_bwd_quant(args, row, col, stream), fn);
+}
+
+bs_status bs_mx_quant_1x32(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x, uint8_t* q_row, int64_t ld_qr,
+                           uint8_t* s_row, int64_t ld_sr, uint8_t* q_col, int64_t ld_qc, uint8_t* s_col,
+                           int64_t ld_sc, hipStream_t stream) {
+    static const char* fn = "bs_mx_quant_1x32";
+    const bool row = q_row || s_row, col = q_col || s_col;
+    const bool empty = R == 0 || C == 0;
+    REQUIRE(x || empty, BS_ERR_NULL, "x is NULL");
+    REQUIRE(!row || (q_row && s_row) || empty, BS_ERR_NULL, "q_row and s_row must both be set or both NULL");
+    REQUIRE(!col || (q_col && s_col) || empty, BS_ERR_NULL, "q_col and s_col must both be set or both NULL");
+    REQUIRE(row || col || empty, BS_ERR_NULL, "no output requested (q_row/s_row and q_col/s_col are all NULL)");
+    REQUIRE(R >= 0 && C >= 0, BS_ERR_SHAPE, "R=%lld C=%lld must be >= 0", (long long)R, (long long)C);
+    REQUIRE(C % 128 == 0, BS_ERR_SHAPE, "C=%lld must be a multiple of 128 (128-column tiles of 32-element blocks)",
+            (long long)C);
+    REQUIRE(!col || R % 128 == 0, BS_ERR_SHAPE, "R=%lld must be a multiple of 128 for the column output",
+            (long long)R);
+    REQUIRE(ld_x >= C && ld_x < kMaxLd, BS_ERR_LAYOUT, "ld_x=%lld must be >= C=%lld and < 2^22", (long long)ld_x,
+            (long long)C);
+    REQUIRE(aligned16(x) && ld_x % 8 == 0, BS_ERR_ALIGN, "x must be 16-byte aligned with ld_x %% 8 == 0");
+    if (row) {
+        REQUIRE(ld_qr >= C && ld_qr < kMaxLd, BS_ERR_LAYOUT, "ld_qr=%lld must be >= C=%lld and < 2^22",
+                (long long)ld_qr, (long long)C);
+        REQUIRE(ld_sr >= R && ld_sr % 16 == 0, BS_ERR_LAYOUT,
+                "ld_sr=%lld must be >= R=%lld and a multiple of 16 (s_row is K-major [C/32][ld_sr] bytes)",
+                (long long)ld_sr, (long long)R);
+        REQUIRE(aligned16(q_row) && ld_qr % 16 == 0 && aligned16(s_row), BS_ERR_ALIGN,
+                "q_row and s_row must be 16-byte aligned with ld_qr %% 16 == 0");
+    }
+    if (col) {
+        REQUIRE(ld_qc >= R && ld_qc < kMaxLd, BS_ERR_LAYOUT, "ld_qc=%lld must be >= R=%lld and < 2^22",
+                (long long)ld_qc, (long long)R);
+        REQUIRE(ld_sc >= C && ld_sc % 16 == 0, BS_ERR_LAYOUT,
+                "ld_sc=%lld must be >= C=%lld and a multiple of 16 (s_col is K-major [R/32][ld_sc] bytes)",
+                (long long)ld_sc, (long long)C);
+        REQUIRE(aligned16(q_col) && ld_qc % 16 == 0 && aligned16(s_col), BS_ERR_ALIGN,
+                "q_col and s_col must be 16-byte aligned with ld_qc %% 16 == 0");
+    }
+    if (empty) return ok();
+    bs::MxQuantArgs a{x, R, C, ld_x, q_row, ld_qr, s_row, ld_sr, q_col, ld_qc, s_col, ld_sc, C / 128};
+    return hip_status(bs::launch_mx_quant(a, row, col, stream), fn);
+}
+
+bs_status bs_mx_scaled_mm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa,
+                          int64_t ld_sa, const uint8_t* b, int64_t ldb, const uint8_t* sb, int64_t ld_sb, void* d,
+                          int64_t ldd, bs_dtype d_dtype, hipStream_t stream) {
+    static const char* fn = "bs_mx_scaled_mm";
+    REQUIRE((a && sa) || M == 0 || K == 0, BS_ERR_NULL, "a and sa must be non-NULL");
+    REQUIRE((b && sb) || N == 0 || K == 0, BS_ERR_NULL, "b and sb must be non-NULL");
+    REQUIRE(d || M == 0 || N == 0, BS_ERR_NULL, "d must be non-NULL");
+    REQUIRE(d_dtype == BS_OUT_BF16 || d_dtype == BS_OUT_F32, BS_ERR_MODE, "d_dtype=%d must be BF16 or F32",
+            (int)d_dtype);
+    REQUIRE(M >= 0 && N >= 0 && K >= 0, BS_ERR_SHAPE, "M, N, K must be >= 0");
+    REQUIRE(N % 128 == 0, BS_ERR_SHAPE, "N=%lld must be a multiple of 128", (long long)N);
+    REQUIRE(K % 128 == 0, BS_ERR_SHAPE, "K=%lld must be a multiple of 128 (four 32-element blocks per K step)",
+            (long long)K);
+    REQUIRE(lda >= K && ldb >= K, BS_ERR_LAYOUT,
+            "lda=%lld, ldb=%lld must be >= K=%lld: a [M, K] and b [N, K] contiguous along the contraction",
+            (long long)lda, (long long)ldb, (long long)K);
+    REQUIRE(ldd >= N, BS_ERR_LAYOUT, "ldd=%lld < N=%lld: d is row-major [M, N]", (long long)ldd, (long long)N);
+    REQUIRE(ld_sa >= M && ld_sa % 16 == 0, BS_ERR_LAYOUT,
+            "ld_sa=%lld must be >= M=%lld and a multiple of 16 (sa is K-major [K/32][ld_sa] bytes)",
+            (long long)ld_sa, (long long)M);
+    REQUIRE(ld_sb >= N && ld_sb % 16 == 0, BS_ERR_LAYOUT,
+            "ld_sb=%lld must be >= N=%lld and a multiple of 16 (sb is K-major [K/32][ld_sb] bytes)",
+            (long long)ld_sb, (long long)N);
+    REQUIRE(lda < (1ll << 22) && ldb < (1ll << 22), BS_ERR_LAYOUT,
+            "lda and ldb must be < 2^22 elements (32-bit tile offsets)");
+    REQUIRE((K / 32 + 1) * (ld_sa > ld_sb ? ld_sa : ld_sb) < (1ll << 31), BS_ERR_LAYOUT,
+            "scale tensors must be smaller than 2 GiB (32-bit offsets)");
+    REQUIRE(aligned16(a) && lda % 16 == 0 && aligned16(b) && ldb % 16 == 0, BS_ERR_ALIGN,
+            "a and b must be 16-byte aligned with lda, ldb %% 16 == 0");
+    REQUIRE(aligned16(sa) && aligned16(sb), BS_ERR_ALIGN, "sa and sb must be 16-byte aligned");
+    REQUIRE(aligned16(d) && ldd % (d_dtype == BS_OUT_F32 ? 4 : 8) == 0, BS_ERR_ALIGN,
+            "d must be 16-byte aligned with 16-byte rows");
+    if (M == 0 || N == 0) return ok();
+    bs::MxGemmArgs g{};
+    g.M = M; g.N = N; g.K = K;
+    g.a = a; g.lda = lda; g.sa = sa; g.ld_sa = ld_sa;
+    g.b = b; g.ldb = ldb; g.sb = sb; g.ld_sb = ld_sb;
+    g.d = d; g.ldd = ldd;
+    return hip_status(bs::launch_mx_gemm(g, d_dtype == BS_OUT_F32, stream), fn);
 }
 
 bs_status bs_quant_128x128(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x, uint8_t* q, int64_t ld_q,

@@ -21,6 +21,7 @@
 // and writes each requested output once.
 #include "bs_kernels.h"
 #include "bs_device.h"
+#include "bs_mx.h"
 
 namespace bs {
 
@@ -465,6 +466,101 @@ __global__ __launch_bounds__(kThreads) void swiglu_bwd_quant_kernel(SwigluBwdArg
     }
 }
 
+// ---- MXFP8 (OCP Microscaling reading): 32-element blocks, E8M0 scales ----
+// E8M0 byte of a block, floor(log2(amax)) - 8 + 127, from amax's exponent
+// field; an amax below 2^-119 (scale exponent under -127), a subnormal amax
+// or zero gives the smallest scale, byte 0.
+__device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
+    const uint32_t ex = (__float_as_uint(amax) >> 23) & 0xFFu;
+    return ex > 8u ? ex - 8u : 0u;
+}
+
+// Four elements divided by 2^(byte - 127) (exact: a power-of-two scaling),
+// saturated at +-448, encoded (round to nearest even, sign kept).
+__device__ __forceinline__ uint32_t mx_encode4(float x0, float x1, float x2, float x3, uint32_t byte) {
+    const int ne = 127 - (int)byte;
+    return encode4(clamp448(__builtin_amdgcn_ldexpf(x0, ne)), clamp448(__builtin_amdgcn_ldexpf(x1, ne)),
+                   clamp448(__builtin_amdgcn_ldexpf(x2, ne)), clamp448(__builtin_amdgcn_ldexpf(x3, ne)));
+}
+
+// MX quantizer over 128x128 tiles: ROW writes 32-element blocks along each
+// row (q_row [R, C], s_row[(c / 32) * ld_sr + r]); COL writes blocks of 32
+// consecutive rows of each column, transposed (q_col [C, R],
+// s_col[(r / 32) * ld_sc + c]).  A row block spans the 4 threads of a lane
+// quad (8 columns each); a column block spans the 4 row groups of one wave.
+template <bool ROW, bool COL>
+__global__ __launch_bounds__(kThreads) void mx_quant_kernel(MxQuantArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t s_tr[COL ? 2 : 1][COL ? kTile * kTile : 16];
+
+    const int t = threadIdx.x;
+    const int tr = t >> 4, tc = t & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int64_t ntiles = ((a.R + kTile - 1) / kTile) * a.col_tiles;
+
+    int64_t tile = blockIdx.x;
+    if (tile >= ntiles) return;
+    const int voff_x = (8 * tr) * (int)(a.ld_x * 2) + 16 * tc;
+    Raw raw;
+    load_raw(a.x, a.ld_x, (tile / a.col_tiles) * kTile, (tile % a.col_tiles) * kTile, a.R, voff_x, raw);
+
+    for (int parity = 0; tile < ntiles; tile += gridDim.x, parity ^= 1) {
+        const int64_t r0 = (tile / a.col_tiles) * kTile, c0 = (tile % a.col_tiles) * kTile;
+        const int64_t rows = (a.R - r0) < kTile ? (a.R - r0) : kTile;
+        TileRegs tl;
+        unpack_tile(raw, tl);
+        const int64_t next = tile + gridDim.x;
+        if (next < ntiles)
+            load_raw(a.x, a.ld_x, (next / a.col_tiles) * kTile, (next % a.col_tiles) * kTile, a.R, voff_x, raw);
+
+        if (ROW) {
+            const __amdgpu_buffer_rsrc_t rq = rsrc(a.q_row + r0 * a.ld_qr + c0, rows * a.ld_qr);
+            const int voff_q = (8 * tr) * (int)a.ld_qr + 8 * tc;
+            // scale bytes of the tile's 4 column blocks (the lane quad of columns 8tc.. shares block tc / 4):
+            // uniform descriptor over the 4 scale rows, the block in the lane offset, rows checked explicitly
+            const __amdgpu_buffer_rsrc_t rs = rsrc(a.s_row + (c0 / 32) * a.ld_sr + r0, 3 * a.ld_sr + rows);
+            const int voff_s = (tc / 4) * (int)a.ld_sr;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float m = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(tl.f[i][j]));
+                uint32_t mb = __float_as_uint(m);
+                mb = max(mb, (uint32_t)__builtin_amdgcn_mov_dpp((int)mb, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+                mb = max(mb, (uint32_t)__builtin_amdgcn_mov_dpp((int)mb, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+                const uint32_t byte = mx_scale_byte(__uint_as_float(mb));
+                const uint32_t lo = mx_encode4(tl.f[i][0], tl.f[i][1], tl.f[i][2], tl.f[i][3], byte);
+                const uint32_t hi = mx_encode4(tl.f[i][4], tl.f[i][5], tl.f[i][6], tl.f[i][7], byte);
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, rq, voff_q, i * (int)a.ld_qr, 0);
+                // one byte store per row: rows past the end are dropped, nothing beyond is written
+                if ((tc & 3) == 0 && 8 * tr + i < rows)
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, rs, voff_s + 8 * tr + i, 0, 0);
+            }
+        }
+        if (COL) {
+            uint2 codes[8];
+            uint32_t bytes[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float m = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(tl.f[i][j]));
+                m = fmaxf(m, __shfl_xor(m, 16));
+                m = fmaxf(m, __shfl_xor(m, 32));
+                bytes[j] = mx_scale_byte(m);
+                codes[j].x = mx_encode4(tl.f[0][j], tl.f[1][j], tl.f[2][j], tl.f[3][j], bytes[j]);
+                codes[j].y = mx_encode4(tl.f[4][j], tl.f[5][j], tl.f[6][j], tl.f[7][j], bytes[j]);
+            }
+            if ((t & 63) < 16) {  // row group 0 of each wave: the 8 columns' scale bytes of the wave's 32 rows
+                const __amdgpu_buffer_rsrc_t rs = rsrc(a.s_col + (r0 / 32 + wave) * a.ld_sc + c0, kTile);
+                const uint32_t w0 = bytes[0] | (bytes[1] << 8) | (bytes[2] << 16) | (bytes[3] << 24);
+                const uint32_t w1 = bytes[4] | (bytes[5] << 8) | (bytes[6] << 16) | (bytes[7] << 24);
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, rs, 8 * tc, 0, 0);
+            }
+            store_transposed(s_tr[parity], codes, tr, tc, a.q_col + c0 * a.ld_qc + r0, a.ld_qc);
+        }
+    }
+}
+
 // 128x128 quantizer.  MODE kQ128Rows writes the codes in place (q, s),
 // kQ128Transposed writes each tile transposed (3-D colwise: q, s), kQ128Both
 // writes both from one read of x (rows to q, s; transposed to qt, st).
@@ -592,6 +688,14 @@ hipError_t launch_swiglu_bwd_quant(const SwigluBwdArgs& a, bool row, bool col, h
     if (row && col) return launch_persistent(swiglu_bwd_quant_kernel<true, true>, a, tiles, stream);
     if (row) return launch_persistent(swiglu_bwd_quant_kernel<true, false>, a, tiles, stream);
     return launch_persistent(swiglu_bwd_quant_kernel<false, true>, a, tiles, stream);
+}
+
+hipError_t launch_mx_quant(const MxQuantArgs& a, bool row, bool col, hipStream_t stream) {
+    const int64_t tiles = ((a.R + kTile - 1) / kTile) * a.col_tiles;
+    if (tiles == 0) return hipSuccess;
+    if (row && col) return launch_persistent(mx_quant_kernel<true, true>, a, tiles, stream);
+    if (row) return launch_persistent(mx_quant_kernel<true, false>, a, tiles, stream);
+    return launch_persistent(mx_quant_kernel<false, true>, a, tiles, stream);
 }
 
 hipError_t launch_quant_128x128(const Quant128Args& a, Quant128Mode mode, hipStream_t stream) {

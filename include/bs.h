@@ -169,6 +169,43 @@ bs_status bs_swiglu_bwd_quant_1x128(const uint16_t* a, const uint16_t* b, const 
                                     hipStream_t stream);
 
 /*
+ * MXFP8 variant (the pages' MXFP8 recipe -- "[mxfp8 moe training] use new 3d
+ * colwise quantization kernel", summary and microbenchmark table -- which the
+ * pages name but do not define; the definition used is the OCP Microscaling
+ * v1.0 one): blocks of 32 consecutive values along the contraction, one E8M0
+ * scale byte per block, 2^(byte - 127) with byte = floor(log2(amax)) - 8 + 127
+ * clamped to [0, 254] (a zero block gets byte 0), elements
+ * e4m3(clamp(x / 2^(byte - 127), -448, 448)).  Scale tensors are bytes,
+ * K-major like the 1x128 ones: s[(k / 32) * ld_s + row], ld_s % 16 == 0.
+ *
+ * bs_mx_quant_1x32 -- one HBM pass producing either or both of
+ *   row output: q_row[r * ld_qr + c], s_row[(c / 32) * ld_sr + r]
+ *   col output: 32 consecutive rows of a column, transposed:
+ *               q_col[c * ld_qc + r], s_col[(r / 32) * ld_sc + c]
+ *   x [R, C] bf16, ld_x >= C; C % 128 == 0; R % 128 == 0 when the col
+ *   output is requested.  ld_qr >= C, ld_sr >= R; ld_qc >= R, ld_sc >= C;
+ *   ld_sr, ld_sc multiples of 16; at least one output pair set.
+ */
+bs_status bs_mx_quant_1x32(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x,
+                           uint8_t* q_row, int64_t ld_qr, uint8_t* s_row, int64_t ld_sr,
+                           uint8_t* q_col, int64_t ld_qc, uint8_t* s_col, int64_t ld_sc,
+                           hipStream_t stream);
+
+/*
+ * bs_mx_scaled_mm -- D[M, N] = A[M, K] . B[N, K]^T with MX scales on both
+ * operands: D = sum_k 2^(sa(m, k/32) - 127) dec(a[m, k]) 2^(sb(n, k/32) - 127)
+ * dec(b[n, k]), fp32 accumulation (gfx950's block-scaled MFMA applies the
+ * scales), bf16 or fp32 output.
+ *   a [M, K] row-major, lda >= K; sa [K/32][ld_sa >= M] bytes
+ *   b [N, K] (contiguous along K), ldb >= K; sb [K/32][ld_sb >= N] bytes
+ *   K % 128 == 0, N % 128 == 0; ld_sa, ld_sb multiples of 16; 16-byte
+ *   aligned operands with lda, ldb multiples of 16.  Errors as bs_scaled_mm.
+ */
+bs_status bs_mx_scaled_mm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa,
+                          int64_t ld_sa, const uint8_t* b, int64_t ldb, const uint8_t* sb, int64_t ld_sb, void* d,
+                          int64_t ldd, bs_dtype d_dtype, hipStream_t stream);
+
+/*
  * bs_quant_128x128 -- weight quantizer, one scale per 128x128 tile.
  *   x [R, C] bf16 (R = out features, C = in features = contraction),
  *   q[r * ld_q + c], s[(c / 128) * ld_s + r / 128].

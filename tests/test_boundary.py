@@ -238,3 +238,66 @@ def test_swiglu_bwd_quant_validation(lib, kw, code, frag):
 
 def test_swiglu_bwd_quant_empty_is_ok(lib):
     assert _swb(lib, R=0, a=None, b=None, dh=None) == OK
+
+
+def _mxq(lib, x=P, R=256, C=512, ld_x=512, q_row=P, ld_qr=512, s_row=P, ld_sr=256, q_col=P, ld_qc=256, s_col=P,
+         ld_sc=512):
+    return lib.bs_mx_quant_1x32(x, R, C, ld_x, q_row, ld_qr, s_row, ld_sr, q_col, ld_qc, s_col, ld_sc, None)
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(x=None), NULL, "x is NULL"),
+    (dict(s_row=None), NULL, "q_row and s_row"),
+    (dict(q_col=None), NULL, "q_col and s_col"),
+    (dict(q_row=None, s_row=None, q_col=None, s_col=None), NULL, "no output requested"),
+    (dict(C=96, ld_x=96, ld_qr=96, ld_sc=96), SHAPE, "multiple of 128"),
+    (dict(R=200, ld_sr=208), SHAPE, "multiple of 128 for the column output"),
+    (dict(ld_x=256), LAYOUT, "ld_x"),
+    (dict(ld_qr=384), LAYOUT, "ld_qr"),
+    (dict(ld_sr=248), LAYOUT, "ld_sr"),
+    (dict(ld_sr=264 + 4), LAYOUT, "multiple of 16"),
+    (dict(ld_qc=128), LAYOUT, "ld_qc"),
+    (dict(ld_sc=500), LAYOUT, "ld_sc"),
+    (dict(x=PU), ALIGN, "x must be 16-byte aligned"),
+    (dict(s_col=PU), ALIGN, "q_col and s_col must be 16-byte aligned"),
+])
+def test_mx_quant_validation(lib, kw, code, frag):
+    assert _mxq(lib, **kw) == code
+    assert frag in lib.bs_last_error().decode()
+
+
+def test_mx_quant_rows_only_skip_the_row_multiple_check(lib):
+    # with only the row output, R=200 passes the shape check and is stopped
+    # by the scale layout (ld_sr not a multiple of 16) before any launch
+    assert _mxq(lib, R=0, x=None, q_col=None, s_col=None) == OK
+    assert _mxq(lib, R=200, ld_sr=200, q_col=None, s_col=None) == LAYOUT   # 200 is not a multiple of 16
+
+
+def _mxmm(lib, M=256, N=512, K=384, a=P, lda=384, sa=P, ld_sa=256, b=P, ldb=384, sb=P, ld_sb=512, d=P, ldd=512,
+          dt=0):
+    return lib.bs_mx_scaled_mm(M, N, K, a, lda, sa, ld_sa, b, ldb, sb, ld_sb, d, ldd, dt, None)
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(a=None), NULL, "a and sa"),
+    (dict(sb=None), NULL, "b and sb"),
+    (dict(d=None), NULL, "d must be non-NULL"),
+    (dict(dt=7), MODE, "d_dtype"),
+    (dict(N=200, ldd=200, ld_sb=208), SHAPE, "N=200"),
+    (dict(K=96, lda=96, ldb=96), SHAPE, "K=96"),
+    (dict(lda=256), LAYOUT, "lda"),
+    (dict(ldd=256), LAYOUT, "ldd"),
+    (dict(ld_sa=128), LAYOUT, "ld_sa"),
+    (dict(ld_sb=520), LAYOUT, "ld_sb"),
+    (dict(a=PU), ALIGN, "a and b must be 16-byte aligned"),
+    (dict(sa=PU), ALIGN, "sa and sb"),
+    (dict(d=PU), ALIGN, "d must be 16-byte aligned"),
+])
+def test_mx_scaled_mm_validation(lib, kw, code, frag):
+    assert _mxmm(lib, **kw) == code
+    assert frag in lib.bs_last_error().decode()
+
+
+def test_mx_scaled_mm_empty_is_ok(lib):
+    assert _mxmm(lib, M=0, a=None, sa=None) == OK
+    assert _mxmm(lib, N=0, ldd=0, b=None, sb=None, d=None) == OK
