@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     bs_diag_division,
     bs_diag_e4m3_census,
     bs_grouped_scaled_mm,
+    bs_mx_grouped_scaled_mm,
     bs_mx_quant_1x32,
     bs_mx_scaled_mm,
     bs_quant_128x128,

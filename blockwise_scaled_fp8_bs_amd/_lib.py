@@ -19,6 +19,8 @@ SIGNATURES = {
                                        _I64, _P, _I64, _P]),
     "bs_mx_quant_1x32": (_E, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P]),
     "bs_mx_scaled_mm": (_E, [_I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _E, _P]),
+    "bs_mx_grouped_scaled_mm": (_E, [_E, _I64, _I64, _I64, _I64, _P, _P, _I64, _P, _I64, _P, _I64, _I64, _P, _I64,
+                                     _I64, _P, _I64, _I64, _E, _P]),
     "bs_quant_128x128": (_E, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P]),
     "bs_quant_3d_colwise": (_E, [_P, _I64, _I64, _I64, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P]),
     "bs_quant_128x128_both": (_E, [_P, _I64, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P, _I64,

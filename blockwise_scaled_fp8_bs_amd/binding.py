@@ -254,6 +254,56 @@ def bs_mx_scaled_mm(a, sa, b, sb, out=None, out_dtype=torch.bfloat16, stream=Non
     return out
 
 
+def bs_mx_grouped_scaled_mm(mode, group_end, a, sa, b, sb, out=None, out_dtype=torch.bfloat16, stream=None):
+    """Grouped (MoE) MX GEMM, group semantics as ``bs_grouped_scaled_mm``.
+
+    BS_GROUP_M: a [M, K], sa [K/32, >= M]; b [G, N, K]; sb [G, K/32, >= N]
+      (uint8, any 16-byte multiple stride between experts); out [M, N].
+    BS_GROUP_K: a [M, T], sa [T/32, >= M]; b [N, T], sb [T/32, >= N];
+      out [G, M, N]; group g contracts over tokens [end_{g-1}, end_g), ends
+      multiples of 128.
+    group_end: int32 GPU tensor [G] of cumulative ends.
+    """
+    _require(group_end is not None and group_end.dtype == torch.int32 and group_end.is_cuda
+             and group_end.dim() == 1, "group_end must be a 1-D int32 GPU tensor")
+    G = group_end.shape[0]
+    _require(group_end.stride(0) == 1 or G <= 1, "group_end must be contiguous")
+    _mat(a, "a", torch.uint8)
+    M, K = a.shape
+    ld_sa = _mx_scale(sa, "sa", K // 32, M)
+    dt_map = {torch.bfloat16: BS_OUT_BF16, torch.float32: BS_OUT_F32}
+    if mode == BS_GROUP_M:
+        _mat(b, "b", torch.uint8, 3)
+        _require(b.shape[0] == G and b.shape[2] == K, f"b must be [{G}, N, {K}]")
+        N = b.shape[1]
+        _mat(sb, "sb", torch.uint8, 3)
+        _require(sb.shape[0] == G and sb.shape[1] == K // 32 and sb.shape[2] >= N,
+                 f"sb must be [{G}, {K // 32}, >= {N}]")
+        if out is None:
+            out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+        _mat(out, "out", out.dtype)
+        _require(tuple(out.shape) == (M, N), f"out must be [{M}, {N}]")
+        args = [mode, G, M, N, K, _ptr(group_end), _ptr(a), _ld(a), _ptr(sa), ld_sa,
+                _ptr(b), b.stride(0), b.stride(1), _ptr(sb), sb.stride(0), sb.stride(1),
+                _ptr(out), 0, _ld(out)]
+    else:
+        _mat(b, "b", torch.uint8)
+        N, Kb = b.shape
+        _require(Kb == K, f"b must be [N, {K}] (tokens contiguous)")
+        ld_sb = _mx_scale(sb, "sb", K // 32, N)
+        if out is None:
+            out = torch.empty((G, M, N), dtype=out_dtype, device=a.device)
+        _mat(out, "out", out.dtype, 3)
+        _require(tuple(out.shape) == (G, M, N), f"out must be [{G}, {M}, {N}]")
+        args = [mode, G, M, N, K, _ptr(group_end), _ptr(a), _ld(a), _ptr(sa), ld_sa,
+                _ptr(b), 0, _ld(b), _ptr(sb), 0, ld_sb,
+                _ptr(out), out.stride(0), out.stride(1)]
+    dt = dt_map.get(out.dtype)
+    _require(dt is not None, "out must be bfloat16 or float32")
+    _check(_lib.load().bs_mx_grouped_scaled_mm(*args, dt, _stream(stream)), "bs_mx_grouped_scaled_mm")
+    return out
+
+
 def bs_quant_128x128(x, q, s, stream=None):
     """128x128 quantizer: x [R, C] bf16 -> q [R, C] uint8, s [C/128, >= R/128]."""
     _mat(x, "x", torch.bfloat16)

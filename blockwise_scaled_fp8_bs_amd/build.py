@@ -32,7 +32,7 @@ CFLAGS = [
     "-I", INCLUDE,
 ]
 
-SOURCES = ["bs_api.hip", "bs_quant.hip", "bs_gemm.hip", "bs_mx_gemm.hip", "bs_diag.hip"]
+SOURCES = ["bs_api.hip", "bs_quant.hip", "bs_gemm.hip", "bs_diag.hip"]
 
 
 def _run(cmd):

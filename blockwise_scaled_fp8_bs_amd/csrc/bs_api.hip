@@ -242,10 +242,12 @@ bs_status bs_mx_quant_1x32(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x
     return hip_status(bs::launch_mx_quant(a, row, col, stream), fn);
 }
 
-bs_status bs_mx_scaled_mm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa,
-                          int64_t ld_sa, const uint8_t* b, int64_t ldb, const uint8_t* sb, int64_t ld_sb, void* d,
-                          int64_t ldd, bs_dtype d_dtype, hipStream_t stream) {
-    static const char* fn = "bs_mx_scaled_mm";
+namespace {
+
+// Argument checks shared by the MX GEMMs (dense and grouped).
+bs_status check_mx_gemm_common(const char* fn, int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
+                               const uint8_t* sa, int64_t ld_sa, const uint8_t* b, int64_t ldb, const uint8_t* sb,
+                               int64_t ld_sb, void* d, int64_t ldd, bs_dtype d_dtype) {
     REQUIRE((a && sa) || M == 0 || K == 0, BS_ERR_NULL, "a and sa must be non-NULL");
     REQUIRE((b && sb) || N == 0 || K == 0, BS_ERR_NULL, "b and sb must be non-NULL");
     REQUIRE(d || M == 0 || N == 0, BS_ERR_NULL, "d must be non-NULL");
@@ -274,13 +276,72 @@ bs_status bs_mx_scaled_mm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int
     REQUIRE(aligned16(sa) && aligned16(sb), BS_ERR_ALIGN, "sa and sb must be 16-byte aligned");
     REQUIRE(aligned16(d) && ldd % (d_dtype == BS_OUT_F32 ? 4 : 8) == 0, BS_ERR_ALIGN,
             "d must be 16-byte aligned with 16-byte rows");
+    return ok();
+}
+
+}  // namespace
+
+bs_status bs_mx_scaled_mm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa,
+                          int64_t ld_sa, const uint8_t* b, int64_t ldb, const uint8_t* sb, int64_t ld_sb, void* d,
+                          int64_t ldd, bs_dtype d_dtype, hipStream_t stream) {
+    static const char* fn = "bs_mx_scaled_mm";
+    bs_status st = check_mx_gemm_common(fn, M, N, K, a, lda, sa, ld_sa, b, ldb, sb, ld_sb, d, ldd, d_dtype);
+    if (st != BS_OK) return st;
     if (M == 0 || N == 0) return ok();
-    bs::MxGemmArgs g{};
+    bs::GemmArgs g{};
     g.M = M; g.N = N; g.K = K;
     g.a = a; g.lda = lda; g.sa = sa; g.ld_sa = ld_sa;
     g.b = b; g.ldb = ldb; g.sb = sb; g.ld_sb = ld_sb;
     g.d = d; g.ldd = ldd;
-    return hip_status(bs::launch_mx_gemm(g, d_dtype == BS_OUT_F32, stream), fn);
+    g.G = 1;
+    g.tiles_m = (M + 255) / 256;
+    g.tiles_n = (N + 255) / 256;
+    g.num_tiles = g.tiles_m * g.tiles_n;
+    return hip_status(bs::launch_gemm(g, bs::kDense, bs::kScaleMx, d_dtype == BS_OUT_F32, stream), fn);
+}
+
+bs_status bs_mx_grouped_scaled_mm(bs_group_mode mode, int64_t G, int64_t M, int64_t N, int64_t K,
+                                  const int32_t* group_end, const uint8_t* a, int64_t lda, const uint8_t* sa,
+                                  int64_t ld_sa, const uint8_t* b, int64_t stride_bg, int64_t ldb, const uint8_t* sb,
+                                  int64_t stride_sbg, int64_t ld_sb, void* d, int64_t stride_dg, int64_t ldd,
+                                  bs_dtype d_dtype, hipStream_t stream) {
+    static const char* fn = "bs_mx_grouped_scaled_mm";
+    REQUIRE(mode == BS_GROUP_M || mode == BS_GROUP_K, BS_ERR_MODE, "mode=%d must be BS_GROUP_M or BS_GROUP_K",
+            (int)mode);
+    REQUIRE(group_end, BS_ERR_NULL, "group_end is NULL");
+    REQUIRE(G >= 0, BS_ERR_SHAPE, "G=%lld must be >= 0", (long long)G);
+    bs_status st = check_mx_gemm_common(fn, M, N, K, a, lda, sa, ld_sa, b, ldb, sb, ld_sb, d, ldd, d_dtype);
+    if (st != BS_OK) return st;
+    bs::GemmArgs g{};
+    g.M = M; g.N = N; g.K = K;
+    g.a = a; g.lda = lda; g.sa = sa; g.ld_sa = ld_sa;
+    g.b = b; g.ldb = ldb; g.sb = sb; g.ld_sb = ld_sb;
+    g.d = d; g.ldd = ldd;
+    g.G = G; g.group_end = group_end;
+    g.tiles_n = (N + 255) / 256;
+    if (mode == BS_GROUP_M) {
+        REQUIRE(stride_dg == 0, BS_ERR_MODE, "BS_GROUP_M writes one D [M, N]: stride_dg must be 0");
+        REQUIRE(stride_bg >= 0 && stride_sbg >= 0, BS_ERR_LAYOUT, "stride_bg and stride_sbg must be >= 0");
+        REQUIRE(stride_bg % 16 == 0 && stride_sbg % 16 == 0, BS_ERR_ALIGN,
+                "stride_bg and stride_sbg must be multiples of 16 bytes");
+        if (G == 0 || M == 0 || N == 0) return ok();
+        g.stride_bg = stride_bg;
+        g.stride_sbg = stride_sbg;
+        g.tiles_m = (M + 255) / 256;
+        g.num_tiles = (g.tiles_m + G) * g.tiles_n;  // upper bound on the sum of per-group tile rows
+        return hip_status(bs::launch_gemm(g, bs::kGroupM, bs::kScaleMx, d_dtype == BS_OUT_F32, stream), fn);
+    }
+    REQUIRE(stride_bg == 0 && stride_sbg == 0, BS_ERR_MODE,
+            "BS_GROUP_K shares one B over the groups: stride_bg and stride_sbg must be 0");
+    REQUIRE(M % 128 == 0, BS_ERR_SHAPE, "M=%lld must be a multiple of 128 for BS_GROUP_K", (long long)M);
+    REQUIRE(G <= 1 || stride_dg >= M * ldd, BS_ERR_LAYOUT, "stride_dg=%lld < M*ldd", (long long)stride_dg);
+    REQUIRE(stride_dg % (d_dtype == BS_OUT_F32 ? 4 : 8) == 0, BS_ERR_ALIGN,
+            "stride_dg must keep every D[g] 16-byte aligned");
+    if (G == 0 || M == 0 || N == 0) return ok();
+    g.stride_dg = stride_dg;
+    g.tiles_m = (M + 255) / 256;
+    g.num_tiles = G * g.tiles_m * g.tiles_n;
+    return hip_status(bs::launch_gemm(g, bs::kGroupK, bs::kScaleMx, d_dtype == BS_OUT_F32, stream), fn);
 }
 
 bs_status bs_quant_128x128(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x, uint8_t* q, int64_t ld_q,
@@ -443,7 +504,8 @@ bs_status bs_scaled_mm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_
     g.tiles_m = (M + 255) / 256;
     g.tiles_n = (N + 255) / 256;
     g.num_tiles = g.tiles_m * g.tiles_n;
-    return hip_status(bs::launch_gemm(g, bs::kDense, b_kind == BS_SCALE_1X128, d_dtype == BS_OUT_F32, stream), fn);
+    return hip_status(bs::launch_gemm(g, bs::kDense, b_kind == BS_SCALE_1X128 ? bs::kScale1x128 : bs::kScale128x128,
+                                      d_dtype == BS_OUT_F32, stream), fn);
 }
 
 bs_status bs_grouped_scaled_mm(bs_group_mode mode, int64_t G, int64_t M, int64_t N, int64_t K,
@@ -482,7 +544,7 @@ bs_status bs_grouped_scaled_mm(bs_group_mode mode, int64_t G, int64_t M, int64_t
         g.stride_sbg = stride_sbg;
         g.tiles_m = (M + 255) / 256;
         g.num_tiles = (g.tiles_m + G) * g.tiles_n;  // upper bound on the sum of per-group tile rows
-        return hip_status(bs::launch_gemm(g, bs::kGroupM, false, d_dtype == BS_OUT_F32, stream), fn);
+        return hip_status(bs::launch_gemm(g, bs::kGroupM, bs::kScale128x128, d_dtype == BS_OUT_F32, stream), fn);
     }
     REQUIRE(b_kind == BS_SCALE_1X128, BS_ERR_MODE,
             "BS_GROUP_K contracts two 1x128-scaled operands (b_kind = BS_SCALE_1X128)");
@@ -498,7 +560,7 @@ bs_status bs_grouped_scaled_mm(bs_group_mode mode, int64_t G, int64_t M, int64_t
     g.stride_dg = stride_dg;
     g.tiles_m = (M + 255) / 256;
     g.num_tiles = G * g.tiles_m * g.tiles_n;
-    return hip_status(bs::launch_gemm(g, bs::kGroupK, true, d_dtype == BS_OUT_F32, stream), fn);
+    return hip_status(bs::launch_gemm(g, bs::kGroupK, bs::kScale1x128, d_dtype == BS_OUT_F32, stream), fn);
 }
 
 bs_status bs_diag_e4m3_census(uint32_t* min_bits, uint32_t* max_bits, unsigned long long* counts,

@@ -3,6 +3,10 @@
 //   D[m, n] = sum_kb sa(m, kb) * sb(n, kb) * P_kb[m, n],
 //   P_kb[m, n] = sum_{k in block kb} dec(A[m, k]) * dec(B[n, k])
 //
+// and the MXFP8 form (E8M0 scales per 32 K values of each row of A and B):
+//
+//   D[m, n] = sum_k 2^ea(m, k/32) dec(A[m, k]) * 2^eb(n, k/32) dec(B[n, k])
+//
 // (pages: "[not for land] float8 blockwise scaling training prototype using
 // deep_gemm", description -- forward/backward GEMMs with 1x128 activation and
 // 128x128 weight scales, and the 1x128 x 1x128 grad_weight GEMM; "add FSDP
@@ -27,6 +31,14 @@
 //    non-temporal.
 //  * Tile ids are remapped so that each of the 8 XCDs works on a contiguous
 //    range of tiles, ordered in groups of 8 tile rows for L2 reuse.
+//  * MX (pages: "[mxfp8 moe training] use new 3d colwise quantization
+//    kernel", summary and microbenchmark table; the format is the OCP MX
+//    v1.0 definition, which the pages do not state): the same kernel with
+//    v_mfma_scale applying the E8M0 bytes itself -- each lane supplies the
+//    byte of its operand row and of one 32-wide K chunk -- so the MFMA
+//    accumulates straight into the fp32 tile and there is no VALU fold.
+//    The scale bytes of a K block (4 chunks x 256 rows per operand, 1 KiB)
+//    ride along with its operand tiles.
 #include "bs_kernels.h"
 
 namespace bs {
@@ -44,14 +56,26 @@ constexpr int WAVES_N = 4;
 constexpr int WM = 128, WN = 64;
 constexpr int TM = WM / 16, TN = WN / 16;
 constexpr int kGroupRows = 8;  // tile rows per L2 group
+constexpr int kChunks = BK / 32;  // MX blocks per K block
+constexpr int kMxPitch = BM + 16;  // MX scale bytes staged per chunk: 256 rows from a 16-byte aligned start
 
 constexpr int kMaxRankedGroups = 256;  // GROUP_K: groups ordered by size up to this count (<= NT)
+
+// Scales of one operand for one K block: fp32 per row (1x128), the two
+// 128x128 block scales of a B tile (f[0], f[1]), or MX bytes [chunk][row]
+// with a pitch of 272: a tile of a grouped A may start at any row, and its
+// bytes are copied from the 16-byte boundary at or below it.
+union ScaleStage {
+    float f[BM];
+    uint8_t e8[kChunks * kMxPitch];
+};
+static_assert(BM == BN, "one scale stage layout serves both operands");
 
 struct __attribute__((aligned(16))) Smem {
     uint8_t a[2][BM * BK];
     uint8_t b[2][BN * BK];
-    float sa[2][BM];
-    float sb[2][BN];
+    ScaleStage sa[2];
+    ScaleStage sb[2];
     int32_t group_by_rank[kMaxRankedGroups];  // GROUP_K: group index of the r-th largest group
     int32_t group_tmp[kMaxRankedGroups];
 };
@@ -180,18 +204,34 @@ struct Operands {
     i32x4 a, b, sa, sb;
 };
 
-template <int KIND, bool B1X128>
+template <int KIND, int SC>
 __device__ __forceinline__ Operands make_operands(const GemmArgs& p, const Tile& t) {
     const int64_t rows_a = (t.m_end - t.m0) < BM ? (t.m_end - t.m0) : BM;
     const int64_t rows_b = (p.N - t.n0) < BN ? (p.N - t.n0) : BN;
     const int64_t nkb_all = p.K / BK;
     const uint8_t* const b = KIND == kGroupM ? p.b + t.g * p.stride_bg : p.b;
-    const float* const sb = KIND == kGroupM ? p.sb + t.g * p.stride_sbg : p.sb;
     Operands o;
     o.a = make_rsrc(p.a + (int64_t)t.m0 * p.lda, rows_a * p.lda);
     o.b = make_rsrc(b + (int64_t)t.n0 * p.ldb, rows_b * p.ldb);
-    o.sa = make_rsrc(p.sa + t.m0, ((nkb_all - 1) * p.ld_sa + (p.M - t.m0)) * 4);
-    if (B1X128) {
+    if (SC == kScaleMx) {
+        // bytes of the tile's rows in every chunk row; the last chunk row is
+        // read up to the 16-byte boundary at or above column M (N): the range
+        // check drops whole dwords, so a limit inside a dword would also drop
+        // the valid bytes before it, and an aligned 16-byte block holding a
+        // valid byte cannot cross a page.  Reads past the tile's valid rows
+        // see other rows' bytes or zero and feed only outputs that are never
+        // stored.
+        const int64_t nch = p.K / 32;
+        const int64_t ma = t.m0 & ~15;  // 16-byte aligned start (ld_sa and the tensor are)
+        const uint8_t* const sa = static_cast<const uint8_t*>(p.sa);
+        const uint8_t* const sb = static_cast<const uint8_t*>(p.sb) + (KIND == kGroupM ? t.g * p.stride_sbg : 0);
+        o.sa = make_rsrc(sa + ma, (nch - 1) * p.ld_sa + ((p.M + 15) & ~15) - ma);
+        o.sb = make_rsrc(sb + t.n0, (nch - 1) * p.ld_sb + ((p.N + 15) & ~15) - t.n0);
+        return o;
+    }
+    const float* const sb = static_cast<const float*>(p.sb) + (KIND == kGroupM ? t.g * p.stride_sbg : 0);
+    o.sa = make_rsrc(static_cast<const float*>(p.sa) + t.m0, ((nkb_all - 1) * p.ld_sa + (p.M - t.m0)) * 4);
+    if (SC == kScale1x128) {
         o.sb = make_rsrc(sb + t.n0, ((nkb_all - 1) * p.ld_sb + (p.N - t.n0)) * 4);
     } else {
         const int64_t nb = t.n0 / BK, nb_count = (p.N + BK - 1) / BK;
@@ -231,10 +271,11 @@ __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" :
 // lane offsets.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-template <int KIND, bool B1X128, bool OUT_F32>
-__global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
-    __shared__ Smem sm;
-
+template <int KIND, int SC, bool OUT_F32>
+__device__ __forceinline__ void gemm_body(const GemmArgs& p) {
+    __shared__ Smem sm;  // one per instantiation; each kernel below uses one
+    constexpr bool B1X128 = SC == kScale1x128;
+    constexpr bool MX = SC == kScaleMx;
     const int t = threadIdx.x;
     const int lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = w / WAVES_N, wn = w % WAVES_N;
@@ -288,7 +329,36 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
     const int voff_a = (int)((w * 8 + ld_lrow) * p.lda) + ld_lchunk * 16;
     const int voff_b = (int)((w * 8 + ld_lrow) * p.ldb) + ld_lchunk * 16;
     const int voff_s = B1X128 ? lane * 16 : lane * 4;
+    // MX scale copies: 4 chunks x 17 pieces of 16 bytes per operand; piece
+    // q of the 68 lands at stage byte 16 q (chunk q / 17 at 272 (q / 17)).
+    // Lanes 0..63 copy pieces 0..63, lanes 0..3 of a second copy pieces 64..67.
+    const int mx_q0 = lane, mx_q1 = 64 + (lane & 3);
+    const int voff_mxa0 = (mx_q0 / 17) * (int)p.ld_sa + (mx_q0 % 17) * 16;
+    const int voff_mxa1 = (mx_q1 / 17) * (int)p.ld_sa + (mx_q1 % 17) * 16;
+    const int voff_mxb0 = (mx_q0 / 17) * (int)p.ld_sb + (mx_q0 % 17) * 16;
+    const int voff_mxb1 = (mx_q1 / 17) * (int)p.ld_sb + (mx_q1 % 17) * 16;
 
+    // The K block's scales, copied by waves w0 (A) and w0 + 1 (B).
+    auto issue_scales = [&](const Operands& o, int32_t kb, int s, int w0) {
+        if (MX) {
+            if (w == w0) {
+                const int so = (int)((int64_t)kb * kChunks * p.ld_sa);
+                dma16(o.sa, lds_addr(&sm.sa[s].e8[0]), voff_mxa0, so);
+                if (lane < 4) dma16(o.sa, lds_addr(&sm.sa[s].e8[1024]), voff_mxa1, so);
+            } else if (w == w0 + 1) {
+                const int so = (int)((int64_t)kb * kChunks * p.ld_sb);
+                dma16(o.sb, lds_addr(&sm.sb[s].e8[0]), voff_mxb0, so);
+                if (lane < 4) dma16(o.sb, lds_addr(&sm.sb[s].e8[1024]), voff_mxb1, so);
+            }
+        } else if (w == w0) {
+            dma16(o.sa, lds_addr(&sm.sa[s].f[0]), lane * 16, (int)((int64_t)kb * p.ld_sa * 4));
+        } else if (w == w0 + 1) {
+            if (B1X128)
+                dma16(o.sb, lds_addr(&sm.sb[s].f[0]), voff_s, (int)((int64_t)kb * p.ld_sb * 4));
+            else if (lane < 2)
+                dma4(o.sb, lds_addr(&sm.sb[s].f[0]), voff_s, (int)((int64_t)kb * p.ld_sb * 4));
+        }
+    };
     auto issue_loads = [&](const Operands& o, int32_t kb, int s) {
         const int k_off = kb * BK;
 #pragma unroll
@@ -296,14 +366,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
             dma16(o.a, lds_addr(&sm.a[s][(8 * i + w) * 1024]), voff_a, k_off + (int)(64 * i * p.lda));
             dma16(o.b, lds_addr(&sm.b[s][(8 * i + w) * 1024]), voff_b, k_off + (int)(64 * i * p.ldb));
         }
-        if (w == 0) {
-            dma16(o.sa, lds_addr(&sm.sa[s][0]), lane * 16, (int)((int64_t)kb * p.ld_sa * 4));
-        } else if (w == 1) {
-            if (B1X128)
-                dma16(o.sb, lds_addr(&sm.sb[s][0]), voff_s, (int)((int64_t)kb * p.ld_sb * 4));
-            else if (lane < 2)
-                dma4(o.sb, lds_addr(&sm.sb[s][0]), voff_s, (int)((int64_t)kb * p.ld_sb * 4));
-        }
+        issue_scales(o, kb, s, 0);
     };
     // The same copies issued by the four waves of group g alone (rows
     // [(4i + w % 4) * 8, +8) in round i = 0..7).  Copies stall the issuing
@@ -321,19 +384,19 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
             dma16(o.a, lds_addr(&sm.a[s][(4 * i + wq) * 1024]), voff_a4, k_off + (int)(32 * i * p.lda));
             dma16(o.b, lds_addr(&sm.b[s][(4 * i + wq) * 1024]), voff_b4, k_off + (int)(32 * i * p.ldb));
         }
-        if (wq == 0) {
-            dma16(o.sa, lds_addr(&sm.sa[s][0]), lane * 16, (int)((int64_t)kb * p.ld_sa * 4));
-        } else if (wq == 1) {
-            if (B1X128)
-                dma16(o.sb, lds_addr(&sm.sb[s][0]), voff_s, (int)((int64_t)kb * p.ld_sb * 4));
-            else if (lane < 2)
-                dma4(o.sb, lds_addr(&sm.sb[s][0]), voff_s, (int)((int64_t)kb * p.ld_sb * 4));
-        }
+        issue_scales(o, kb, s, 4 * g);
     };
+    // An MFMA operand fragment: the MFMA reads a lane's first four registers
+    // as K = 16 lg .. 16 lg + 15 and its last four as K = 64 + 16 lg .. (a
+    // layout measured on gfx950 with one nonzero byte per call), so lane
+    // group lg loads logical chunks lg and 4 + lg of the row and K inside
+    // the MFMA is K in memory -- which the MX scales need (lane group c
+    // supplies the scale of K = 32 c .. 32 c + 31); the 128-block forms
+    // would accept any K order common to both operands.
     auto frag = [&](const uint8_t* base, int row) -> v8i {
         const int sw = swz(row);
-        const uint4 lo = *reinterpret_cast<const uint4*>(base + row * BK + (((2 * lg) ^ sw) * 16));
-        const uint4 hi = *reinterpret_cast<const uint4*>(base + row * BK + (((2 * lg + 1) ^ sw) * 16));
+        const uint4 lo = *reinterpret_cast<const uint4*>(base + row * BK + ((lg ^ sw) * 16));
+        const uint4 hi = *reinterpret_cast<const uint4*>(base + row * BK + (((lg + 4) ^ sw) * 16));
         v8i r;
         r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
         r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
@@ -342,7 +405,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
 
     Tile cur;
     resolve_tile<KIND>(p, idx, total, rows_total, sm.group_by_rank, cur);
-    Operands ops = make_operands<KIND, B1X128>(p, cur);
+    Operands ops = make_operands<KIND, SC>(p, cur);
     int32_t nkb = cur.kb1 - cur.kb0;
     int s = 0;  // LDS stage holding the current K block
     if (nkb > 0) issue_loads(ops, cur.kb0, 0);
@@ -360,7 +423,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
         bool next_resolved = false;
         auto load_next = [&](int stage) {
             resolve_tile<KIND>(p, nidx, total, rows_total, sm.group_by_rank, nxt);
-            nops = make_operands<KIND, B1X128>(p, nxt);
+            nops = make_operands<KIND, SC>(p, nxt);
             if (nxt.kb1 > nxt.kb0) issue_loads(nops, nxt.kb0, stage);
             next_resolved = true;
         };
@@ -389,48 +452,70 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
             v8i bf[TN];
 #pragma unroll
             for (int j = 0; j < TN; ++j) bf[j] = frag(lb, wn * WN + j * 16 + lr);
-            v4f sbv[TN];  // B scale of each of the lane's output columns
-            if (B1X128) {
+            if (MX) {
+                // E8M0 bytes of the lane's operand rows in K chunk lg (A's
+                // tile rows start cur.m0 % 16 bytes into the staged chunk)
+                const uint8_t* const ea = &sm.sa[s].e8[lg * kMxPitch + (cur.m0 & 15) + wm * WM + lr];
+                const uint8_t* const eb = &sm.sb[s].e8[lg * kMxPitch + wn * WN + lr];
+                int scb[TN], sca[TM];
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const float4 t4 = *reinterpret_cast<const float4*>(&sm.sb[s][wn * WN + j * 16 + 4 * lg]);
-                    sbv[j] = v4f{t4.x, t4.y, t4.z, t4.w};
+                for (int j = 0; j < TN; ++j) scb[j] = eb[j * 16];
+#pragma unroll
+                for (int i = 0; i < TM; ++i) sca[i] = ea[i * 16];
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    const v8i af = af_next;
+                    if (i + 1 < TM) af_next = frag(la, wm * WM + (i + 1) * 16 + lr);
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], 0, 0, 0,
+                                                                                      scb[j], 0, sca[i]);
                 }
-            }
-            const float sbw = B1X128 ? 0.f : sm.sb[s][wn >> 1];
-            float sa_i[TM];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) sa_i[i] = sm.sa[s][wm * WM + i * 16 + lr];
-
-            // Software pipeline at MFMA granularity: the scale fmas of tile
-            // (i, j) run while the MFMA of the next tile executes.
-            v4f pbuf[2];
-            int pi = 0, pj = 0;
-            auto fold = [&](const v4f& pk, int i, int j) {
+            } else {
+                v4f sbv[TN];  // B scale of each of the lane's output columns
                 if (B1X128) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        acc[i][j][r] = __builtin_fmaf(pk[r], sa_i[i] * sbv[j][r], acc[i][j][r]);
-                } else {
-                    const float sc = sa_i[i] * sbw;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pk[r], sc, acc[i][j][r]);
+                    for (int j = 0; j < TN; ++j) {
+                        const float4 t4 = *reinterpret_cast<const float4*>(&sm.sb[s].f[wn * WN + j * 16 + 4 * lg]);
+                        sbv[j] = v4f{t4.x, t4.y, t4.z, t4.w};
+                    }
                 }
-            };
+                const float sbw = B1X128 ? 0.f : sm.sb[s].f[wn >> 1];
+                float sa_i[TM];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const v8i af = af_next;
-                if (i + 1 < TM) af_next = frag(la, wm * WM + (i + 1) * 16 + lr);
+                for (int i = 0; i < TM; ++i) sa_i[i] = sm.sa[s].f[wm * WM + i * 16 + lr];
+
+                // Software pipeline at MFMA granularity: the scale fmas of tile
+                // (i, j) run while the MFMA of the next tile executes.
+                v4f pbuf[2];
+                int pi = 0, pj = 0;
+                auto fold = [&](const v4f& pk, int i, int j) {
+                    if (B1X128) {
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int q = i * TN + j;
-                    pbuf[q & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, zero, 0, 0, 0, 0, 0, 0);
-                    if (q > 0) fold(pbuf[(q - 1) & 1], pi, pj);
-                    pi = i;
-                    pj = j;
+                        for (int r = 0; r < 4; ++r)
+                            acc[i][j][r] = __builtin_fmaf(pk[r], sa_i[i] * sbv[j][r], acc[i][j][r]);
+                    } else {
+                        const float sc = sa_i[i] * sbw;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pk[r], sc, acc[i][j][r]);
+                    }
+                };
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    const v8i af = af_next;
+                    if (i + 1 < TM) af_next = frag(la, wm * WM + (i + 1) * 16 + lr);
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        const int q = i * TN + j;
+                        pbuf[q & 1] =
+                            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, zero, 0, 0, 0, 0, 0, 0);
+                        if (q > 0) fold(pbuf[(q - 1) & 1], pi, pj);
+                        pi = i;
+                        pj = j;
+                    }
                 }
+                fold(pbuf[(TM * TN - 1) & 1], TM - 1, TN - 1);
             }
-            fold(pbuf[(TM * TN - 1) & 1], TM - 1, TN - 1);
             wait_dma();
             __syncthreads();
             s ^= 1;
@@ -494,6 +579,16 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
     }
 }
 
+template <int KIND, bool B1X128, bool OUT_F32>
+__global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
+    gemm_body<KIND, B1X128 ? kScale1x128 : kScale128x128, OUT_F32>(p);
+}
+
+template <int KIND, bool OUT_F32>
+__global__ __launch_bounds__(NT) void mx_gemm_kernel(GemmArgs p) {
+    gemm_body<KIND, kScaleMx, OUT_F32>(p);
+}
+
 // Persistent grid: as many workgroups as fit on the device at once, never
 // more than the tiles.
 template <typename Kern>
@@ -509,27 +604,36 @@ unsigned persistent_grid(Kern kernel, int64_t tiles) {
     return (unsigned)(tiles < cap ? tiles : cap);
 }
 
-template <int KIND, bool B1, bool F32>
-hipError_t launch_one(const GemmArgs& a, hipStream_t stream) {
-    const unsigned grid = persistent_grid(gemm_kernel<KIND, B1, F32>, a.num_tiles);
-    hipLaunchKernelGGL((gemm_kernel<KIND, B1, F32>), dim3(grid), dim3(NT), 0, stream, a);
+template <typename Kern>
+hipError_t launch_persistent_gemm(Kern kernel, const GemmArgs& a, hipStream_t stream) {
+    const unsigned grid = persistent_grid(kernel, a.num_tiles);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int KIND>
-hipError_t launch_kind(const GemmArgs& a, bool b_1x128, bool out_f32, hipStream_t stream) {
+hipError_t launch_kind(const GemmArgs& a, ScaleMode scales, bool out_f32, hipStream_t stream) {
     if (a.num_tiles <= 0) return hipSuccess;
-    if (b_1x128) return out_f32 ? launch_one<KIND, true, true>(a, stream) : launch_one<KIND, true, false>(a, stream);
-    return out_f32 ? launch_one<KIND, false, true>(a, stream) : launch_one<KIND, false, false>(a, stream);
+    switch (scales) {
+        case kScaleMx:
+            return out_f32 ? launch_persistent_gemm(mx_gemm_kernel<KIND, true>, a, stream)
+                           : launch_persistent_gemm(mx_gemm_kernel<KIND, false>, a, stream);
+        case kScale1x128:
+            return out_f32 ? launch_persistent_gemm(gemm_kernel<KIND, true, true>, a, stream)
+                           : launch_persistent_gemm(gemm_kernel<KIND, true, false>, a, stream);
+        default:
+            return out_f32 ? launch_persistent_gemm(gemm_kernel<KIND, false, true>, a, stream)
+                           : launch_persistent_gemm(gemm_kernel<KIND, false, false>, a, stream);
+    }
 }
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs& a, GroupKind kind, bool b_1x128, bool out_f32, hipStream_t stream) {
+hipError_t launch_gemm(const GemmArgs& a, GroupKind kind, ScaleMode scales, bool out_f32, hipStream_t stream) {
     switch (kind) {
-        case kDense: return launch_kind<kDense>(a, b_1x128, out_f32, stream);
-        case kGroupM: return launch_kind<kGroupM>(a, b_1x128, out_f32, stream);
-        default: return launch_kind<kGroupK>(a, b_1x128, out_f32, stream);
+        case kDense: return launch_kind<kDense>(a, scales, out_f32, stream);
+        case kGroupM: return launch_kind<kGroupM>(a, scales, out_f32, stream);
+        default: return launch_kind<kGroupK>(a, scales, out_f32, stream);
     }
 }
 

@@ -65,15 +65,20 @@ enum Quant128Mode { kQ128Rows = 0, kQ128Transposed = 1, kQ128Both = 2 };
 
 enum GroupKind { kDense = 0, kGroupM = 1, kGroupK = 2 };
 
+// Scales of a GEMM's operands: A 1x128 with B 128x128 or B 1x128 (fp32,
+// folded per 128-block), or MX on both (E8M0 per 32 elements, applied by
+// the scaled MFMA).
+enum ScaleMode { kScale128x128 = 0, kScale1x128 = 1, kScaleMx = 2 };
+
 struct GemmArgs {
     int64_t M, N, K;
     const uint8_t* a;
     int64_t lda;
-    const float* sa;
+    const void* sa;  // fp32 1x128 scales, or E8M0 bytes [K/32][ld_sa] (kScaleMx)
     int64_t ld_sa;
     const uint8_t* b;
     int64_t ldb;
-    const float* sb;
+    const void* sb;  // fp32 128x128 or 1x128 scales, or E8M0 bytes [K/32][ld_sb] (kScaleMx)
     int64_t ld_sb;
     void* d;
     int64_t ldd;
@@ -90,8 +95,7 @@ hipError_t launch_quant_1x128(const Quant1x128Args& a, bool row, bool col, bool 
 hipError_t launch_quant_128x128(const Quant128Args& a, Quant128Mode mode, hipStream_t stream);
 hipError_t launch_swiglu_bwd_quant(const SwigluBwdArgs& a, bool row, bool col, hipStream_t stream);
 
-// b_1x128: B scales per row (wgrad) instead of per 128x128 block.
-hipError_t launch_gemm(const GemmArgs& a, GroupKind kind, bool b_1x128, bool out_f32, hipStream_t stream);
+hipError_t launch_gemm(const GemmArgs& a, GroupKind kind, ScaleMode scales, bool out_f32, hipStream_t stream);
 
 hipError_t launch_diag_e4m3_census(uint32_t* min_bits, uint32_t* max_bits, unsigned long long* counts,
                                    hipStream_t stream);

@@ -206,6 +206,29 @@ bs_status bs_mx_scaled_mm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int
                           int64_t ldd, bs_dtype d_dtype, hipStream_t stream);
 
 /*
+ * bs_mx_grouped_scaled_mm -- the MoE form of bs_mx_scaled_mm, with the group
+ * semantics of bs_grouped_scaled_mm (pages: "[mxfp8 moe training] use new 3d
+ * colwise quantization kernel", microbenchmark table -- MXFP8 grouped GEMMs
+ * over (M, N, K, G)).  group_end as there: DEVICE int32[G], cumulative,
+ * clamped on the device, never read on the host.
+ *   BS_GROUP_M (forward, dgrad): rows [end_{g-1}, end_g) of A use expert g,
+ *     whose B is b + g*stride_bg ([N, K], ldb) with scale bytes
+ *     sb + g*stride_sbg ([K/32][ld_sb >= N]); stride_bg and stride_sbg
+ *     multiples of 16; stride_dg must be 0; any group sizes.
+ *   BS_GROUP_K (wgrad): contraction groups, ends multiples of 128; stride_bg
+ *     and stride_sbg must be 0; D_g = d + g*stride_dg; M % 128 == 0; an
+ *     empty group writes zeros.
+ * Other arguments and errors as bs_mx_scaled_mm.
+ */
+bs_status bs_mx_grouped_scaled_mm(bs_group_mode mode, int64_t G, int64_t M, int64_t N, int64_t K,
+                                  const int32_t* group_end,
+                                  const uint8_t* a, int64_t lda, const uint8_t* sa, int64_t ld_sa,
+                                  const uint8_t* b, int64_t stride_bg, int64_t ldb,
+                                  const uint8_t* sb, int64_t stride_sbg, int64_t ld_sb,
+                                  void* d, int64_t stride_dg, int64_t ldd, bs_dtype d_dtype,
+                                  hipStream_t stream);
+
+/*
  * bs_quant_128x128 -- weight quantizer, one scale per 128x128 tile.
  *   x [R, C] bf16 (R = out features, C = in features = contraction),
  *   q[r * ld_q + c], s[(c / 128) * ld_s + r / 128].

@@ -301,3 +301,31 @@ def test_mx_scaled_mm_validation(lib, kw, code, frag):
 def test_mx_scaled_mm_empty_is_ok(lib):
     assert _mxmm(lib, M=0, a=None, sa=None) == OK
     assert _mxmm(lib, N=0, ldd=0, b=None, sb=None, d=None) == OK
+
+
+def _mxg(lib, mode=0, G=2, M=256, N=512, K=384, ge=P, a=P, lda=384, sa=P, ld_sa=256, b=P, stride_bg=512 * 384,
+         ldb=384, sb=P, stride_sbg=12 * 512, ld_sb=512, d=P, stride_dg=0, ldd=512, dt=0):
+    return lib.bs_mx_grouped_scaled_mm(mode, G, M, N, K, ge, a, lda, sa, ld_sa, b, stride_bg, ldb, sb, stride_sbg,
+                                       ld_sb, d, stride_dg, ldd, dt, None)
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(mode=7), MODE, "mode=7"),
+    (dict(ge=None), NULL, "group_end is NULL"),
+    (dict(G=-1), SHAPE, "G=-1"),
+    (dict(ld_sa=200), LAYOUT, "ld_sa"),
+    (dict(stride_dg=4096), MODE, "stride_dg must be 0"),
+    (dict(stride_sbg=-16), LAYOUT, "stride_bg and stride_sbg must be >= 0"),
+    (dict(stride_sbg=520), ALIGN, "multiples of 16"),
+    (dict(mode=1, stride_bg=0, stride_sbg=0, M=200, ld_sa=208, stride_dg=200 * 512), SHAPE, "M=200"),
+    (dict(mode=1, stride_sbg=0, stride_dg=256 * 512), MODE, "shares one B"),
+    (dict(mode=1, stride_bg=0, stride_sbg=0, stride_dg=1024), LAYOUT, "stride_dg"),
+])
+def test_mx_grouped_validation(lib, kw, code, frag):
+    assert _mxg(lib, **kw) == code
+    assert frag in lib.bs_last_error().decode()
+
+
+def test_mx_grouped_empty_is_ok(lib):
+    assert _mxg(lib, G=0) == OK
+    assert _mxg(lib, mode=1, G=0, stride_bg=0, stride_sbg=0) == OK

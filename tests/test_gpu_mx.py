@@ -170,6 +170,14 @@ def _operand(rows, K, sigma, seed):
     return mx.quant_mx_rowwise(bits16(inputs.bf16_normal((rows, K), sigma, seed)))
 
 
+def _normal_codes(rows, K, rng, sigma=64.0):
+    """E4M3 codes of N(0, sigma) values (saturated at 448), drawn directly.
+    (Uniformly random bytes are heavy-tailed: a dot product can then come
+    within a factor of two of ||a|| ||b||, where a bf16 output's own rounding
+    exceeds the bound.)"""
+    return e4m3.encode(np.clip(rng.standard_normal((rows, K)) * sigma, -448, 448).astype(np.float32))
+
+
 def _check(d_gpu, qa, sa, qb, sb, exact=False):
     a = mx.dequant_mx(qa, sa)
     b = mx.dequant_mx(qb, sb)
@@ -184,7 +192,7 @@ def _check(d_gpu, qa, sa, qb, sb, exact=False):
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 256, 512), (384, 640, 768), (300, 384, 640), (512, 128, 1024),
-                                   (64, 256, 128)])
+                                   (64, 256, 128), (301, 256, 256)])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_mx_scaled_mm(M, N, K, out_dtype):
     need_gpu()
@@ -262,12 +270,10 @@ def test_mx_scaled_mm_full_size_sampled():
     need_gpu()
     M, N, K = 8192, 4096, 4096
     rng = np.random.default_rng(21)
-    qa = rng.integers(0, 256, (M, K)).astype(np.uint8)
-    qb = rng.integers(0, 256, (N, K)).astype(np.uint8)
-    qa[(qa & 0x7F) == 0x7F] = 0
-    qb[(qb & 0x7F) == 0x7F] = 0
-    sa = rng.integers(117, 138, (M, K // 32)).astype(np.uint8)
-    sb = rng.integers(117, 138, (N, K // 32)).astype(np.uint8)
+    qa = _normal_codes(M, K, rng)
+    qb = _normal_codes(N, K, rng)
+    sa = rng.integers(125, 131, (M, K // 32)).astype(np.uint8)   # bf16 output: scales within 2^5
+    sb = rng.integers(125, 131, (N, K // 32)).astype(np.uint8)
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     print("mx_scaled_mm 8192 x 4096 x 4096", flush=True)
     bs.bs_mx_scaled_mm(torch.from_numpy(qa).cuda(), _to_gpu_mx_scales(sa), torch.from_numpy(qb).cuda(),
@@ -280,3 +286,124 @@ def test_mx_scaled_mm_full_size_sampled():
     d = out[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
     ok, worst = gemm.check_close(d, ref, a, b)
     assert ok, f"worst |err| / bound = {worst}"
+
+
+def test_mx_persistent_many_tiles():
+    # 18 x 16 = 288 tiles over at most 256 workgroups, ragged last tile row:
+    # workgroups walk several tiles, prefetching across tile boundaries.
+    # float32 output: with per-block scales spread over 2^15 a row is
+    # dominated by a few blocks, a product can come close to ||a|| ||b||, and
+    # a bf16 output's own rounding (up to 2^-8 |d|) would exceed the bound
+    need_gpu()
+    M, N, K = 4452, 4096, 256
+    rng = np.random.default_rng(31)
+    qa = _normal_codes(M, K, rng)
+    qb = _normal_codes(N, K, rng)
+    sa = rng.integers(120, 135, (M, K // 32)).astype(np.uint8)
+    sb = rng.integers(120, 135, (N, K // 32)).astype(np.uint8)
+    full, out = guarded(M, N, torch.float32)
+    print("mx_scaled_mm persistent 4452 x 4096 x 256", flush=True)
+    bs.bs_mx_scaled_mm(torch.from_numpy(qa).cuda(), _to_gpu_mx_scales(sa), torch.from_numpy(qb).cuda(),
+                       _to_gpu_mx_scales(sb), out=out)
+    torch.cuda.synchronize()
+    _check(out, qa, sa, qb, sb)
+    check_canaries(full, M, N)
+
+
+# ---- grouped (MoE) ----
+
+def _expert_scales(sb_list, interleaved):
+    """Per-expert logical scales [N, K/32] -> a [G, K/32, >= N] uint8 GPU view:
+    stacked tensors, or one [K/32, G*N] matrix viewed per expert."""
+    G = len(sb_list)
+    N, nch = sb_list[0].shape
+    if interleaved:
+        whole = _to_gpu_mx_scales(np.concatenate(sb_list, axis=0))
+        return torch.as_strided(whole, (G, nch, N), (N, whole.stride(0), 1))
+    return torch.stack([_to_gpu_mx_scales(s) for s in sb_list])
+
+
+@pytest.mark.parametrize("sizes,interleaved", [((128, 0, 256), False), ((200, 56, 300), True),
+                                               ((0, 0, 512), False), ((37, 0, 219, 100), True),
+                                               ((1000, 3000, 17, 500), False)])
+def test_mx_group_m(sizes, interleaved):
+    # group starts at any row (37, 256, 356, 1017, ...): the A scale bytes of
+    # a tile are copied from the 16-byte boundary below its first row; M = 4517
+    # ends the scale rows inside a dword
+    need_gpu()
+    G, N, K = len(sizes), 384, 640
+    ends = np.cumsum(sizes).astype(np.int32)
+    M = int(ends[-1])
+    qa, sa = _operand(M, K, 1.0, seed=M + G)
+    ops = [_operand(N, K, 0.02, seed=G + 100 + g) for g in range(G)]
+    qb = torch.from_numpy(np.stack([q for q, _ in ops])).cuda()
+    sb = _expert_scales([s for _, s in ops], interleaved)
+    full, out = guarded(M, N, torch.bfloat16)
+    print(f"mx group_m sizes={sizes} interleaved={interleaved}", flush=True)
+    bs.bs_mx_grouped_scaled_mm(bs.BS_GROUP_M, torch.from_numpy(ends).cuda(), torch.from_numpy(qa).cuda(),
+                               _to_gpu_mx_scales(sa), qb, sb, out=out)
+    torch.cuda.synchronize()
+    d = out.float().cpu().numpy().astype(np.float64)
+    start = 0
+    for g, e in enumerate(ends):
+        if e > start:
+            a = mx.dequant_mx(qa[start:e], sa[start:e])
+            b = mx.dequant_mx(*ops[g])
+            ok, worst = gemm.check_close(d[start:e], a @ b.T, a, b)
+            assert ok, f"group {g}: worst {worst}"
+        start = e
+    check_canaries(full, M, N)
+
+
+@pytest.mark.parametrize("sizes", [(256, 0, 128), (128, 128, 128, 128), (0, 384)])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_mx_group_k(sizes, out_dtype):
+    need_gpu()
+    G, M, N = len(sizes), 256, 384
+    ends = np.cumsum(sizes).astype(np.int32)
+    T = int(ends[-1])
+    qa, sa = _operand(M, T, 0.01, seed=T + 1)   # grad_out^T [M, T]
+    qb, sb = _operand(N, T, 1.0, seed=T + 2)    # x^T [N, T]
+    out_full = torch.full((G + 1, M, N), 5.0, dtype=out_dtype, device="cuda")
+    out = out_full[:G]
+    print(f"mx group_k sizes={sizes} {out_dtype}", flush=True)
+    bs.bs_mx_grouped_scaled_mm(bs.BS_GROUP_K, torch.from_numpy(ends).cuda(), torch.from_numpy(qa).cuda(),
+                               _to_gpu_mx_scales(sa), torch.from_numpy(qb).cuda(), _to_gpu_mx_scales(sb), out=out)
+    torch.cuda.synchronize()
+    d = out.float().cpu().numpy().astype(np.float64)
+    start = 0
+    for g, e in enumerate(ends):
+        if e == start:
+            assert np.all(d[g] == 0), f"empty group {g} must be zeros"
+        else:
+            a = mx.dequant_mx(qa[:, start:e], sa[:, start // 32:e // 32])
+            b = mx.dequant_mx(qb[:, start:e], sb[:, start // 32:e // 32])
+            ok, worst = gemm.check_close(d[g], a @ b.T, a, b)
+            assert ok, f"group {g}: worst {worst}"
+        start = e
+    assert torch.all(out_full[G] == 5.0)
+
+
+def test_mx_group_m_equals_dense_per_group():
+    # bit-for-bit: a group's rows of the grouped product equal the dense MX
+    # product of those rows with the group's expert (same kernel arithmetic)
+    need_gpu()
+    sizes = (300, 212, 500)
+    G, N, K = 3, 256, 512
+    ends = np.cumsum(sizes).astype(np.int32)
+    M = int(ends[-1])
+    qa, sa = _operand(M, K, 1.0, seed=5)
+    ops = [_operand(N, K, 0.05, seed=50 + g) for g in range(G)]
+    qb = torch.from_numpy(np.stack([q for q, _ in ops])).cuda()
+    sb = _expert_scales([s for _, s in ops], False)
+    print("mx group_m vs dense", flush=True)
+    d = bs.bs_mx_grouped_scaled_mm(bs.BS_GROUP_M, torch.from_numpy(ends).cuda(), torch.from_numpy(qa).cuda(),
+                                   _to_gpu_mx_scales(sa), qb, sb, out_dtype=torch.float32)
+    start = 0
+    for g, e in enumerate(ends):
+        dg = bs.bs_mx_scaled_mm(torch.from_numpy(np.ascontiguousarray(qa[start:e])).cuda(),
+                                _to_gpu_mx_scales(sa[start:e]), qb[g], _to_gpu_mx_scales(ops[g][1]),
+                                out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(d[start:e], dg), f"group {g}"
+        start = e
