@@ -31,3 +31,4 @@ from .binding import (  # noqa: F401
 )
 from .linear import Float8BlockwiseLinear, float8_blockwise_linear, swap_linear_layers  # noqa: F401,E402
 from .ffn import Float8BlockwiseGatedFFN, float8_blockwise_gated_ffn  # noqa: F401,E402
+from .mx import Float8MXLinear, float8_mx_linear, mx_grouped_mm  # noqa: F401,E402

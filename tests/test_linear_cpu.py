@@ -84,3 +84,51 @@ def test_gated_ffn_module_shapes_and_conversion():
     assert torch.equal(m.w2, lin[1].weight.detach().to(torch.bfloat16))
     with pytest.raises(ValueError, match="biases"):
         bs.Float8BlockwiseGatedFFN.from_linears(torch.nn.Linear(256, 512), lin[1], lin[2])
+
+
+# ---- the MXFP8 layers: argument checks (no GPU needed) ----
+
+def test_mx_linear_rejects_bad_arguments():
+    w = torch.zeros((256, 384), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="tokens = 100"):
+        bs.float8_mx_linear(torch.zeros((100, 384), dtype=torch.bfloat16), w)
+    with pytest.raises(ValueError, match="out_features = 96"):
+        bs.float8_mx_linear(torch.zeros((128, 384), dtype=torch.bfloat16), torch.zeros((96, 384), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="bfloat16"):
+        bs.float8_mx_linear(torch.zeros((128, 384)), w)
+    with pytest.raises(ValueError, match="contiguous"):
+        bs.float8_mx_linear(torch.zeros((128, 768), dtype=torch.bfloat16)[:, :384], w)
+    with pytest.raises(ValueError, match="features"):
+        bs.float8_mx_linear(torch.zeros((128, 256), dtype=torch.bfloat16), w)
+    with pytest.raises(ValueError, match="GPU"):
+        bs.float8_mx_linear(torch.zeros((128, 384), dtype=torch.bfloat16), w)
+    with pytest.raises(ValueError, match="in_features = 200"):
+        bs.Float8MXLinear(200, 128)
+    with pytest.raises(ValueError, match="bias"):
+        bs.Float8MXLinear.from_linear(torch.nn.Linear(128, 128))
+
+
+def test_mx_grouped_mm_rejects_bad_arguments():
+    x = torch.zeros((512, 256), dtype=torch.bfloat16)
+    w = torch.zeros((4, 384, 256), dtype=torch.bfloat16)
+    ends = torch.tensor([128, 256, 384, 512], dtype=torch.int32)
+    with pytest.raises(ValueError, match="3-D"):
+        bs.mx_grouped_mm(x, w[0], ends)
+    with pytest.raises(ValueError, match=r"x must be \[M, 256\]"):
+        bs.mx_grouped_mm(torch.zeros((512, 128), dtype=torch.bfloat16), w, ends)
+    with pytest.raises(ValueError, match="group_end"):
+        bs.mx_grouped_mm(x, w, ends.long())
+    with pytest.raises(ValueError, match="group_end"):
+        bs.mx_grouped_mm(x, w, ends[:3])
+    with pytest.raises(ValueError, match="tokens = 500"):
+        bs.mx_grouped_mm(torch.zeros((500, 256), dtype=torch.bfloat16), w, ends)
+    with pytest.raises(ValueError, match="GPU"):
+        bs.mx_grouped_mm(x, w, ends)
+
+
+def test_mx_linear_module_conversion():
+    lin = torch.nn.Linear(256, 128, bias=False)
+    m = bs.Float8MXLinear.from_linear(lin)
+    assert m.weight.dtype == torch.bfloat16 and tuple(m.weight.shape) == (128, 256)
+    assert torch.equal(m.weight, lin.weight.detach().to(torch.bfloat16))
+    assert "mxfp8" in repr(m)
