@@ -257,6 +257,66 @@ def ffn_module_timing(M, D, H, median_ms, seed):
             "fused_tflops": round(flops / (f_ms * 1e-3) / 1e12, 1)}
 
 
+# MXFP8 grouped GEMM shapes (tokens M, out N, in K, experts G) and the pages'
+# own MXFP8 and bf16 timings for them, in microseconds, forward and forward +
+# backward ("[mxfp8 moe training] use new 3d colwise quantization kernel",
+# microbenchmark table; another machine's numbers, quoted as context).
+MX_SHAPES = [
+    ((16384, 8192, 5120, 1), {"mxfp8_fwd": 790.56, "mxfp8_fwd_bwd": 2928.22, "bf16_fwd": 1236.03,
+                              "bf16_fwd_bwd": 4257.76}),
+    ((128000, 8192, 5120, 8), {"mxfp8_fwd": 5816.16, "mxfp8_fwd_bwd": 25204.8, "bf16_fwd": 10200.0,
+                               "bf16_fwd_bwd": 44263.5}),
+    ((16384, 2048, 7168, 1), {"mxfp8_fwd": 396.224, "mxfp8_fwd_bwd": 1436.51, "bf16_fwd": 425.248,
+                              "bf16_fwd_bwd": 1458.74}),
+]
+
+
+def mx_grouped_timing(median_ms, seed):
+    """Median forward and forward + backward times of mx_grouped_mm (bf16 in,
+    quantization included, as the pages' op) and of torch bf16 GEMMs per
+    expert, at the pages' microbenchmark shapes with equal-size groups."""
+    rows = []
+    for (M, N, K, G), pages in MX_SHAPES:
+        x = inputs.bf16_normal((M, K), 1.0, seed + 40, device="cuda").requires_grad_()
+        wt = inputs.bf16_normal((G, N, K), 0.02, seed + 41, device="cuda").requires_grad_()
+        dy = inputs.bf16_normal((M, N), 0.01, seed + 42, device="cuda")
+        ends = torch.tensor([(g + 1) * M // G for g in range(G)], dtype=torch.int32, device="cuda")
+        bounds = [0] + ends.tolist()
+
+        def mx_fwd():
+            with torch.no_grad():
+                bs.mx_grouped_mm(x, wt, ends)
+
+        def mx_fwd_bwd():
+            x.grad = wt.grad = None
+            bs.mx_grouped_mm(x, wt, ends).backward(dy)
+
+        def bf16_fwd():
+            with torch.no_grad():
+                for g in range(G):
+                    torch.mm(x[bounds[g]:bounds[g + 1]], wt[g].t())
+
+        def bf16_fwd_bwd():
+            x.grad = wt.grad = None
+            y = torch.cat([torch.mm(x[bounds[g]:bounds[g + 1]], wt[g].t()) for g in range(G)])
+            y.backward(dy)
+
+        t = {name: median_ms(fn, 5) for name, fn in (("mxfp8_fwd", mx_fwd), ("mxfp8_fwd_bwd", mx_fwd_bwd),
+                                                     ("bf16_fwd", bf16_fwd), ("bf16_fwd_bwd", bf16_fwd_bwd))}
+        flops = 2.0 * M * N * K
+        rows.append({"M": M, "N": N, "K": K, "G": G,
+                     "us": {k: round(v * 1e3, 1) for k, v in t.items()},
+                     "mxfp8_fwd_tflops": round(flops / (t["mxfp8_fwd"] * 1e-3) / 1e12, 1),
+                     "mxfp8_fwd_bwd_tflops": round(3 * flops / (t["mxfp8_fwd_bwd"] * 1e-3) / 1e12, 1),
+                     "speedup_vs_bf16": {"fwd": round(t["bf16_fwd"] / t["mxfp8_fwd"], 3),
+                                         "fwd_bwd": round(t["bf16_fwd_bwd"] / t["mxfp8_fwd_bwd"], 3)},
+                     "pages_us": pages})
+        x.grad = wt.grad = None
+        del x, wt, dy
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,6 +326,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ffn-module", action="store_true", help="skip the gated FFN module timing")
+    ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 grouped GEMM timings")
     ap.add_argument("--no-fusion", action="store_true",
                     help="skip the fused gated-activation timings (keeps per-kernel profiles to the step's shapes)")
     ap.add_argument("--cpu-rows", type=int, default=8192,
@@ -474,6 +535,12 @@ def main():
         ffn = ffn_module_timing(w.M, w.K, w.N, median_ms, args.seed)
         torch.cuda.empty_cache()
 
+    # MXFP8 grouped GEMMs (the pages' MoE recipe) at the pages' shapes,
+    # forward and forward + backward with quantization, next to bf16
+    mxfp8 = None
+    if not args.no_mx:
+        mxfp8 = mx_grouped_timing(median_ms, args.seed)
+
     cpu = None
     if not args.no_cpu_baseline:
         tflops, secs, desc = cpu_oracle_sample(w, rows=min(args.cpu_rows, w.M), seed=args.seed)
@@ -506,6 +573,7 @@ def main():
         "swiglu_quant_fusion": fusion,
         "swiglu_bwd_quant_fusion": fusion_bwd,
         "gated_ffn_module": ffn,
+        "mxfp8_grouped_mm": mxfp8,
         "quant_frac_of_copy": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / copy_gbs, 4),
         "kernels": per_kernel,
         "roofline": roofline,

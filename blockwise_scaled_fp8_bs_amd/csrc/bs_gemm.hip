@@ -60,6 +60,7 @@ constexpr int kChunks = BK / 32;  // MX blocks per K block
 constexpr int kMxPitch = BM + 16;  // MX scale bytes staged per chunk: 256 rows from a 16-byte aligned start
 
 constexpr int kMaxRankedGroups = 256;  // GROUP_K: groups ordered by size up to this count (<= NT)
+constexpr int kMaxSlicedGroups = 64;   // GROUP_M: XCD-sliced tile-row order up to this count (8 x 64 <= NT)
 
 // Scales of one operand for one K block: fp32 per row (1x128), the two
 // 128x128 block scales of a B tile (f[0], f[1]), or MX bytes [chunk][row]
@@ -78,6 +79,16 @@ struct __attribute__((aligned(16))) Smem {
     ScaleStage sb[2];
     int32_t group_by_rank[kMaxRankedGroups];  // GROUP_K: group index of the r-th largest group
     int32_t group_tmp[kMaxRankedGroups];
+    // GROUP_M slice order: tile rows before slot k = (slice k / G of group
+    // k % G), and each group's first row, end row and tile rows
+    int32_t slice_start[8 * kMaxSlicedGroups + 1];
+    int32_t g_start[kMaxSlicedGroups], g_end[kMaxSlicedGroups], g_rows[kMaxSlicedGroups];
+    int32_t wave_sum[NT / 64];
+};
+
+// Read-only views of the GROUP_M slice tables (LDS).
+struct SliceTables {
+    const int32_t *slice_start, *g_start, *g_end, *g_rows;
 };
 
 __device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t n) {
@@ -126,7 +137,7 @@ __device__ __forceinline__ int64_t tile_total(const GemmArgs& p, int64_t& rows) 
 
 template <int KIND>
 __device__ __forceinline__ void resolve_tile(const GemmArgs& p, int64_t idx, int64_t total, int64_t rows,
-                                             const int32_t* group_by_rank, Tile& t) {
+                                             const int32_t* group_by_rank, const SliceTables& st, Tile& t) {
     t.g = 0;
     t.kb0 = 0;
     t.kb1 = (int32_t)(p.K / BK);
@@ -137,6 +148,26 @@ __device__ __forceinline__ void resolve_tile(const GemmArgs& p, int64_t idx, int
         t.m0 = (int32_t)(tm * BM);
         t.m_end = (int32_t)p.M;
         t.n0 = (int32_t)(tn * BN);
+    } else if (KIND == kGroupM && p.G <= kMaxSlicedGroups) {
+        // slice order: the largest slot k with slice_start[k] <= tr holds
+        // tile row tr (empty slots share their successor's start).  LDS
+        // reads land in vector registers: readfirstlane keeps the tile
+        // (and the buffer descriptors built from it) in scalar registers.
+        auto lds = [](const int32_t* a, int i) { return __builtin_amdgcn_readfirstlane(a[i]); };
+        int64_t tr, tn;
+        grouped_order(L, rows, p.tiles_n, tr, tn);
+        int lo = 0, hi = 8 * (int)p.G - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (lds(st.slice_start, mid) <= tr) lo = mid;
+            else hi = mid - 1;
+        }
+        const int x = lo / (int)p.G, g = lo - x * (int)p.G;
+        const int64_t row = x * (int64_t)lds(st.g_rows, g) / 8 + (tr - lds(st.slice_start, lo));
+        t.m0 = (int32_t)(lds(st.g_start, g) + row * BM);
+        t.m_end = lds(st.g_end, g);
+        t.n0 = (int32_t)(tn * BN);
+        t.g = g;
     } else if (KIND == kGroupM) {
         int64_t tr, tn;
         grouped_order(L, rows, p.tiles_n, tr, tn);
@@ -286,6 +317,50 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
     int64_t idx = blockIdx.x;
     if (idx >= total) return;
 
+    if (KIND == kGroupM && p.G <= kMaxSlicedGroups) {
+        // Tile-row order for GROUP_M: slice x (of 8) of every group in turn,
+        // x-major.  Each XCD walks a contiguous eighth of the order, so the
+        // 8 XCDs go through the groups together and read one or two
+        // experts' B at a time from the shared last-level cache -- rather
+        // than 8 experts' B at once, which does not fit and streams from
+        // HBM.  Slot k = x * G + g holds rows [x r_g / 8, (x + 1) r_g / 8)
+        // of group g's r_g tile rows.
+        const int t0 = threadIdx.x;
+        if (t0 < p.G) {
+            int64_t s0 = 0, e = 0;
+            for (int h = 0; h <= t0; ++h) {
+                s0 = e;
+                const int64_t v = p.group_end[h];
+                e = v < s0 ? s0 : (v > p.M ? p.M : v);
+            }
+            sm.g_start[t0] = (int32_t)s0;
+            sm.g_end[t0] = (int32_t)e;
+            sm.g_rows[t0] = (int32_t)((e - s0 + BM - 1) / BM);
+        }
+        __syncthreads();
+        const int nslots = 8 * (int)p.G;
+        int32_t v = 0;
+        if (t0 < nslots) {
+            const int x = t0 / (int)p.G, g = t0 - x * (int)p.G;
+            const int64_t r = sm.g_rows[g];
+            v = (int32_t)((x + 1) * r / 8 - x * r / 8);
+        }
+        // block-wide inclusive scan: within each wave, then across waves
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int32_t u = __shfl_up(v, d);
+            if (lane >= d) v += u;
+        }
+        if (lane == 63) sm.wave_sum[w] = v;
+        __syncthreads();
+        int32_t off = 0;
+        for (int i = 0; i < w; ++i) off += sm.wave_sum[i];
+        if (t0 < nslots) sm.slice_start[t0 + 1] = v + off;
+        if (t0 == 0) sm.slice_start[0] = 0;
+        __syncthreads();
+    }
+    const SliceTables slices{sm.slice_start, sm.g_start, sm.g_end, sm.g_rows};
+
     if (KIND == kGroupK && p.G <= kMaxRankedGroups) {
         // Rank the groups by size, largest first (ties: lower index first);
         // thread g handles group g.  Sizes come from the clamped cumulative
@@ -404,7 +479,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
     };
 
     Tile cur;
-    resolve_tile<KIND>(p, idx, total, rows_total, sm.group_by_rank, cur);
+    resolve_tile<KIND>(p, idx, total, rows_total, sm.group_by_rank, slices, cur);
     Operands ops = make_operands<KIND, SC>(p, cur);
     int32_t nkb = cur.kb1 - cur.kb0;
     int s = 0;  // LDS stage holding the current K block
@@ -422,7 +497,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
         Operands nops = ops;
         bool next_resolved = false;
         auto load_next = [&](int stage) {
-            resolve_tile<KIND>(p, nidx, total, rows_total, sm.group_by_rank, nxt);
+            resolve_tile<KIND>(p, nidx, total, rows_total, sm.group_by_rank, slices, nxt);
             nops = make_operands<KIND, SC>(p, nxt);
             if (nxt.kb1 > nxt.kb0) issue_loads(nops, nxt.kb0, stage);
             next_resolved = true;

@@ -326,3 +326,35 @@ def test_group_k_more_groups_than_ranked():
             ok, worst = gemm.check_close(d[g], a @ b.T, a, b)
             assert ok, f"group {g}: worst {worst}"
         start = e
+
+
+@pytest.mark.parametrize("G", [64, 70])
+def test_group_m_many_groups(G):
+    """GROUP_M at the largest group count ordered in XCD slices (64) and
+    beyond it (70, the plain group order): ragged and empty groups."""
+    need_gpu()
+    rng = np.random.default_rng(G)
+    sizes = rng.choice([0, 1, 37, 128, 300], G)
+    ends = np.cumsum(sizes).astype(np.int32)
+    M, N, K = int(ends[-1]), 256, 256
+    qa, sa = operand_1x128(M, K, 1.0, seed=G + 1)
+    w = inputs.bf16_normal((G * N, K), 0.02, seed=G + 2)
+    qw, sw = quant.quant_128x128(bits16(w))
+    sw_gpu = to_gpu_scales(sw)
+    sb_view = torch.as_strided(sw_gpu, (G, K // 128, N // 128), (N // 128, sw_gpu.stride(0), 1))
+    qb = torch.from_numpy(qw).cuda().view(G, N, K)
+    full, out = guarded(M, N, torch.bfloat16)
+    print(f"group_m G={G} M={M}", flush=True)
+    bs.bs_grouped_scaled_mm(bs.BS_GROUP_M, torch.from_numpy(ends).cuda(), torch.from_numpy(qa).cuda(),
+                            to_gpu_scales(sa), qb, sb_view, bs.BS_SCALE_128X128, out=out)
+    torch.cuda.synchronize()
+    d = out.float().cpu().numpy().astype(np.float64)
+    start = 0
+    for g, e in enumerate(ends):
+        if e > start:
+            a = gemm.dequant(qa[start:e], sa[start:e], 1)
+            b = gemm.dequant(qw[g * N:(g + 1) * N], sw[g * N // 128:(g + 1) * N // 128], 128)
+            ok, worst = gemm.check_close(d[start:e], a @ b.T, a, b)
+            assert ok, f"group {g}: worst {worst}"
+        start = e
+    check_canaries(full, M, N)

@@ -407,3 +407,32 @@ def test_mx_group_m_equals_dense_per_group():
         torch.cuda.synchronize()
         assert torch.equal(d[start:e], dg), f"group {g}"
         start = e
+
+
+@pytest.mark.parametrize("G", [64, 70])
+def test_mx_group_m_many_groups(G):
+    # the largest group count ordered in XCD slices (64) and beyond (70)
+    need_gpu()
+    rng = np.random.default_rng(G + 7)
+    sizes = rng.choice([0, 1, 37, 128, 300], G)
+    ends = np.cumsum(sizes).astype(np.int32)
+    M, N, K = int(ends[-1]), 256, 256
+    qa, sa = _operand(M, K, 1.0, seed=G)
+    ops = [_operand(N, K, 0.02, seed=1000 + g) for g in range(G)]
+    qb = torch.from_numpy(np.stack([q for q, _ in ops])).cuda()
+    sb = _expert_scales([s for _, s in ops], True)
+    full, out = guarded(M, N, torch.bfloat16)
+    print(f"mx group_m G={G} M={M}", flush=True)
+    bs.bs_mx_grouped_scaled_mm(bs.BS_GROUP_M, torch.from_numpy(ends).cuda(), torch.from_numpy(qa).cuda(),
+                               _to_gpu_mx_scales(sa), qb, sb, out=out)
+    torch.cuda.synchronize()
+    d = out.float().cpu().numpy().astype(np.float64)
+    start = 0
+    for g, e in enumerate(ends):
+        if e > start:
+            a = mx.dequant_mx(qa[start:e], sa[start:e])
+            b = mx.dequant_mx(*ops[g])
+            ok, worst = gemm.check_close(d[start:e], a @ b.T, a, b)
+            assert ok, f"group {g}: worst {worst}"
+        start = e
+    check_canaries(full, M, N)
