@@ -64,8 +64,10 @@ KERNEL_SYMBOL = {
 # while these are unchanged)
 KERNEL_SOURCES = {
     "gemm_kernel": ["bs_gemm.hip", "bs_kernels.h"],
-    "quant_": ["bs_quant.hip", "bs_device.h", "bs_kernels.h"],
-    "swiglu_bwd_quant_kernel": ["bs_quant.hip", "bs_device.h", "bs_kernels.h"],
+    "mx_gemm_kernel": ["bs_gemm.hip", "bs_kernels.h"],
+    "quant_": ["bs_quant.hip", "bs_device.h", "bs_kernels.h", "bs_mx.h"],
+    "swiglu_bwd_quant_kernel": ["bs_quant.hip", "bs_device.h", "bs_kernels.h", "bs_mx.h"],
+    "mx_quant_kernel": ["bs_quant.hip", "bs_device.h", "bs_kernels.h", "bs_mx.h"],
 }
 
 

@@ -399,10 +399,19 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
     // logical chunk (l % 8) ^ swz(row); swz sees bits 0..3 of the row, i.e.
     // l / 8 and the parity of w).  Loop-invariant lane offsets; the K block
     // and the round's 64-row step enter through the uniform soffset.
+    // Logical chunk c holds the row's 16-byte chunk c of K, except for MX:
+    // the MFMA reads a lane's first four registers as K = 16 lg .. 16 lg + 15
+    // and its last four as K = 64 + 16 lg .. (measured on gfx950 with one
+    // nonzero byte per call), and the scale of lane group c covers
+    // K = 32 c .. 32 c + 31, so for MX logical chunk c holds K chunk
+    // (c >> 1) + 4 (c & 1): the fragment reads (logical chunks 2 lg, 2 lg + 1)
+    // then hand the MFMA K in memory order.  (Reading chunks lg and lg + 4
+    // instead costs 3-5 % on every GEMM.)
     const int ld_lrow = lane >> 3;
     const int ld_lchunk = (lane & 7) ^ swz(w * 8 + ld_lrow);
-    const int voff_a = (int)((w * 8 + ld_lrow) * p.lda) + ld_lchunk * 16;
-    const int voff_b = (int)((w * 8 + ld_lrow) * p.ldb) + ld_lchunk * 16;
+    const int ld_kchunk = MX ? (ld_lchunk >> 1) + 4 * (ld_lchunk & 1) : ld_lchunk;
+    const int voff_a = (int)((w * 8 + ld_lrow) * p.lda) + ld_kchunk * 16;
+    const int voff_b = (int)((w * 8 + ld_lrow) * p.ldb) + ld_kchunk * 16;
     const int voff_s = B1X128 ? lane * 16 : lane * 4;
     // MX scale copies: 4 chunks x 17 pieces of 16 bytes per operand; piece
     // q of the 68 lands at stage byte 16 q (chunk q / 17 at 272 (q / 17)).
@@ -449,8 +458,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
     // 16 cycles); with one group issuing per K block, the other group's
     // waves go straight to their MFMAs and keep the matrix pipes busy.
     const int wq = w & 3;
-    const int voff_a4 = (int)((wq * 8 + ld_lrow) * p.lda) + ld_lchunk * 16;
-    const int voff_b4 = (int)((wq * 8 + ld_lrow) * p.ldb) + ld_lchunk * 16;
+    const int voff_a4 = (int)((wq * 8 + ld_lrow) * p.lda) + ld_kchunk * 16;
+    const int voff_b4 = (int)((wq * 8 + ld_lrow) * p.ldb) + ld_kchunk * 16;
     auto issue_loads_group = [&](const Operands& o, int32_t kb, int s, int g) {
         if ((w >> 2) != g) return;
         const int k_off = kb * BK;
@@ -461,17 +470,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
         }
         issue_scales(o, kb, s, 4 * g);
     };
-    // An MFMA operand fragment: the MFMA reads a lane's first four registers
-    // as K = 16 lg .. 16 lg + 15 and its last four as K = 64 + 16 lg .. (a
-    // layout measured on gfx950 with one nonzero byte per call), so lane
-    // group lg loads logical chunks lg and 4 + lg of the row and K inside
-    // the MFMA is K in memory -- which the MX scales need (lane group c
-    // supplies the scale of K = 32 c .. 32 c + 31); the 128-block forms
-    // would accept any K order common to both operands.
+    // An MFMA operand fragment: logical chunks 2 lg and 2 lg + 1 of the row
+    // (for MX, K chunks lg and lg + 4: see the copies above).
     auto frag = [&](const uint8_t* base, int row) -> v8i {
         const int sw = swz(row);
-        const uint4 lo = *reinterpret_cast<const uint4*>(base + row * BK + ((lg ^ sw) * 16));
-        const uint4 hi = *reinterpret_cast<const uint4*>(base + row * BK + (((lg + 4) ^ sw) * 16));
+        const uint4 lo = *reinterpret_cast<const uint4*>(base + row * BK + (((2 * lg) ^ sw) * 16));
+        const uint4 hi = *reinterpret_cast<const uint4*>(base + row * BK + (((2 * lg + 1) ^ sw) * 16));
         v8i r;
         r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
         r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
