@@ -273,12 +273,14 @@ MX_SHAPES = [
 ]
 
 
-def mx_grouped_timing(median_ms, seed):
+def mx_grouped_timing(median_ms, seed, which=None):
     """Median forward and forward + backward times of mx_grouped_mm (bf16 in,
     quantization included, as the pages' op) and of torch bf16 GEMMs per
     expert, at the pages' microbenchmark shapes with equal-size groups."""
     rows = []
-    for (M, N, K, G), pages in MX_SHAPES:
+    for i, ((M, N, K, G), pages) in enumerate(MX_SHAPES):
+        if which is not None and i not in which:
+            continue
         x = inputs.bf16_normal((M, K), 1.0, seed + 40, device="cuda").requires_grad_()
         wt = inputs.bf16_normal((G, N, K), 0.02, seed + 41, device="cuda").requires_grad_()
         dy = inputs.bf16_normal((M, N), 0.01, seed + 42, device="cuda")
@@ -329,6 +331,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ffn-module", action="store_true", help="skip the gated FFN module timing")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 grouped GEMM timings")
+    ap.add_argument("--mx-shapes", default=None,
+                    help="comma-separated indices into the MXFP8 shape list (default: all)")
     ap.add_argument("--no-fusion", action="store_true",
                     help="skip the fused gated-activation timings (keeps per-kernel profiles to the step's shapes)")
     ap.add_argument("--cpu-rows", type=int, default=8192,
@@ -541,7 +545,8 @@ def main():
     # forward and forward + backward with quantization, next to bf16
     mxfp8 = None
     if not args.no_mx:
-        mxfp8 = mx_grouped_timing(median_ms, args.seed)
+        which = None if args.mx_shapes is None else {int(i) for i in args.mx_shapes.split(",")}
+        mxfp8 = mx_grouped_timing(median_ms, args.seed, which)
 
     cpu = None
     if not args.no_cpu_baseline:
