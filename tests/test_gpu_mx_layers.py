@@ -140,3 +140,39 @@ def test_mx_grouped_mm_equals_dense_per_expert():
         assert torch.equal(xg.grad[start:e], xe.grad), f"dx group {g}"
         assert torch.equal(wg.grad[g], we.grad), f"dW group {g}"
         start = e
+
+
+def test_mx_grouped_mm_full_size_sampled():
+    # the bench's MoE shape and launch configuration (128000 tokens, 8 experts
+    # of [8192, 5120], equal groups); sampled outputs recomputed by the oracle
+    # from the bf16 inputs: rows of y and dx in two groups (the expert's W
+    # quantized whole, rows and columns), and single elements of dW (a column
+    # of dy and of x quantized along the group's tokens)
+    need_gpu()
+    M, N, K, G = 128000, 8192, 5120, 8
+    x = inputs.bf16_normal((M, K), 1.0, 61, device="cuda").requires_grad_()
+    w = inputs.bf16_normal((G, N, K), 0.02, 62, device="cuda").requires_grad_()
+    dy = inputs.bf16_normal((M, N), 0.01, 63, device="cuda")
+    ends = torch.tensor([(g + 1) * M // G for g in range(G)], dtype=torch.int32, device="cuda")
+    print("mx grouped mm 128000 x 8192 x 5120, 8 experts", flush=True)
+    y = bs.mx_grouped_mm(x, w, ends)
+    y.backward(dy)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    per = M // G
+    for g in (0, 5):
+        rows = np.sort(rng.choice(per, 6, replace=False)) + g * per
+        idx = torch.from_numpy(rows).cuda()
+        wb = bits16(w[g])
+        xb, gb = bits16(x.detach()[idx]), bits16(dy[idx])
+        ref, a, b = _oracle_mm(mx.quant_mx_rowwise(xb), mx.quant_mx_rowwise(wb))
+        _close(y[idx], ref, a, b, f"y group {g}")
+        ref, a, b = _oracle_mm(mx.quant_mx_rowwise(gb), mx.quant_mx_colwise(wb))
+        _close(x.grad[idx], ref, a, b, f"dx group {g}")
+        lo, hi = g * per, (g + 1) * per
+        for _ in range(4):
+            n, k = int(rng.integers(N)), int(rng.integers(K))
+            qa = mx.quant_mx_rowwise(bits16(dy[lo:hi, n][None]))
+            qb = mx.quant_mx_rowwise(bits16(x.detach()[lo:hi, k][None]))
+            ref, a, b = _oracle_mm(qa, qb)
+            _close(w.grad[g, n, k].reshape(1, 1), ref, a, b, f"dW[{g}, {n}, {k}]")
