@@ -176,7 +176,11 @@ bs_status bs_swiglu_bwd_quant_1x128(const uint16_t* a, const uint16_t* b, const 
  * scale byte per block, 2^(byte - 127) with byte = floor(log2(amax)) - 8 + 127
  * clamped to [0, 254] (a zero block gets byte 0), elements
  * e4m3(clamp(x / 2^(byte - 127), -448, 448)).  Scale tensors are bytes,
- * K-major like the 1x128 ones: s[(k / 32) * ld_s + row], ld_s % 16 == 0.
+ * K-major like the 1x128 ones: s[(k / 32) * ld_s + row], ld_s % 16 == 0
+ * and 16-byte aligned.  The GEMMs read scale bytes in aligned 16-byte
+ * blocks: in each scale row they may read (and never use) the bytes between
+ * the last row (M or N) and the next multiple of 16, which a tensor of
+ * ld_s >= roundup16(rows) holds.
  *
  * bs_mx_quant_1x32 -- one HBM pass producing either or both of
  *   row output: q_row[r * ld_qr + c], s_row[(c / 32) * ld_sr + r]
