@@ -470,6 +470,26 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
         }
         issue_scales(o, kb, s, 4 * g);
     };
+    // Piece k of issue_loads_group's copies for wave group g: k < 16 one
+    // operand copy (A for even k, B for odd k, round k / 2), k == 16 the scales.
+    auto issue_piece = [&](const Operands& o, int32_t kb, int s, int g, int k) {
+        const int k_off = kb * BK;
+        const int i = k >> 1;
+        if (k == 16)
+            issue_scales(o, kb, s, 4 * g);
+        else if ((k & 1) == 0)
+            dma16(o.a, lds_addr(&sm.a[s][(4 * i + wq) * 1024]), voff_a4, k_off + (int)(32 * i * p.lda));
+        else
+            dma16(o.b, lds_addr(&sm.b[s][(4 * i + wq) * 1024]), voff_b4, k_off + (int)(32 * i * p.ldb));
+    };
+    // With 128x128 B scales (forward and dgrad) the issuing group spreads
+    // its copies over its first 9 MFMAs, two per MFMA, instead of issuing
+    // all 17 before them: its waves then join the matrix pipes early, and
+    // every copy is still issued in the first quarter of the K block (3-4 %
+    // faster on the dense and FFN shapes).  The 1x128 x 1x128 kernel needs
+    // its registers for the per-element fold and keeps the block issue; so
+    // does the MX kernel (no gain measured).
+    constexpr bool kSpread = !MX && !B1X128 && KIND != kGroupK;
     // An MFMA operand fragment: logical chunks 2 lg and 2 lg + 1 of the row
     // (for MX, K chunks lg and lg + 4: see the copies above).
     auto frag = [&](const uint8_t* base, int row) -> v8i {
@@ -517,8 +537,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
             for (int j = 0; j < TN; ++j) acc[i][j] = zero;
 
         for (int32_t it = 0; it < nkb; ++it) {
+            const bool spread = kSpread && it + 1 < nkb && (w >> 2) == (it & 1);
             if (it + 1 < nkb) {
-                issue_loads_group(ops, cur.kb0 + it + 1, s ^ 1, it & 1);
+                if (!kSpread) issue_loads_group(ops, cur.kb0 + it + 1, s ^ 1, it & 1);
             } else if (has_next) {
                 load_next(s ^ 1);
             }
@@ -588,6 +609,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
                         const int q = i * TN + j;
                         pbuf[q & 1] =
                             __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, zero, 0, 0, 0, 0, 0, 0);
+                        if (kSpread && q <= 8 && spread) {
+                            issue_piece(ops, cur.kb0 + it + 1, s ^ 1, it & 1, 2 * q);
+                            if (q < 8) issue_piece(ops, cur.kb0 + it + 1, s ^ 1, it & 1, 2 * q + 1);
+                        }
                         if (q > 0) fold(pbuf[(q - 1) & 1], pi, pj);
                         pi = i;
                         pj = j;
