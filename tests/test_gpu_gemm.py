@@ -266,6 +266,64 @@ def test_persistent_group_m_many_tiles():
     check_canaries(full, M, N)
 
 
+@pytest.mark.parametrize("kind", [bs.BS_SCALE_128X128, bs.BS_SCALE_1X128])
+def test_persistent_dense_exact_many_k_blocks(kind):
+    """More tiles than workgroups, 8 K blocks per tile, ragged last tile row,
+    small-integer codes and power-of-two scales (every partial sum exact in
+    fp32): a K block read from the wrong LDS stage, a copy issued for the
+    wrong block or tile, or a scale of the wrong block shows as a bit
+    mismatch against the float64 oracle."""
+    need_gpu()
+    rng = np.random.default_rng(5)
+    M, N, K = 4452, 4096, 1024          # 18 x 16 = 288 tiles
+    qa = rng.choice(SMALL_INT_CODES, size=(M, K))
+    qb = rng.choice(SMALL_INT_CODES, size=(N, K))
+    sa = np.exp2(rng.integers(-2, 3, size=(M, K // 128))).astype(np.float32)
+    rb = 128 if kind == bs.BS_SCALE_128X128 else 1
+    sb = np.exp2(rng.integers(-2, 3, size=(N // rb, K // 128))).astype(np.float32)
+    full, out = guarded(M, N, torch.float32)
+    print(f"persistent exact dense {M}x{N}x{K} kind={kind}", flush=True)
+    bs.bs_scaled_mm(torch.from_numpy(qa).cuda(), to_gpu_scales(sa), torch.from_numpy(qb).cuda(),
+                    to_gpu_scales(sb), kind, out=out)
+    torch.cuda.synchronize()
+    check_result(out, qa, sa, qb, sb, rb, exact=True)
+    check_canaries(full, M, N)
+
+
+def test_persistent_group_m_exact_many_k_blocks():
+    """GROUP_M with ragged and empty groups, more tiles than workgroups and 8 K
+    blocks per tile, on exact small-integer arithmetic: every group's rows
+    must equal the float64 oracle bit for bit."""
+    need_gpu()
+    rng = np.random.default_rng(6)
+    sizes = (700, 0, 1300, 128, 0, 900, 601, 371)
+    G, N, K = len(sizes), 4096, 1024                 # 21 tile rows x 16 = 336 tiles
+    ends = np.cumsum(sizes).astype(np.int32)
+    M = int(ends[-1])
+    qa = rng.choice(SMALL_INT_CODES, size=(M, K))
+    sa = np.exp2(rng.integers(-2, 3, size=(M, K // 128))).astype(np.float32)
+    qw = rng.choice(SMALL_INT_CODES, size=(G * N, K))
+    sw = np.exp2(rng.integers(-2, 3, size=(G * N // 128, K // 128))).astype(np.float32)
+    sw_gpu = to_gpu_scales(sw)
+    sb_view = torch.as_strided(sw_gpu, (G, K // 128, N // 128), (N // 128, sw_gpu.stride(0), 1))
+    full, out = guarded(M, N, torch.float32)
+    print(f"persistent exact group_m sizes={sizes} K={K}", flush=True)
+    bs.bs_grouped_scaled_mm(bs.BS_GROUP_M, torch.from_numpy(ends).cuda(), torch.from_numpy(qa).cuda(),
+                            to_gpu_scales(sa), torch.from_numpy(qw).cuda().view(G, N, K), sb_view,
+                            bs.BS_SCALE_128X128, out=out)
+    torch.cuda.synchronize()
+    d = out.cpu().numpy().astype(np.float64)
+    start = 0
+    for g, e in enumerate(ends):
+        if e > start:
+            a = gemm.dequant(qa[start:e], sa[start:e], 1)
+            b = gemm.dequant(qw[g * N:(g + 1) * N], sw[g * N // 128:(g + 1) * N // 128], 128)
+            bad = np.argwhere(d[start:e] != a @ b.T)
+            assert bad.size == 0, f"group {g}: {len(bad)} inexact elements, first {bad[0]}"
+        start = e
+    check_canaries(full, M, N)
+
+
 def test_persistent_group_k_many_tiles():
     need_gpu()
     # 20 groups of 16 tiles each (320 tiles); empty groups sit between
