@@ -7,6 +7,7 @@ import pytest
 import torch
 
 import blockwise_scaled_fp8_bs_amd as bs
+from blockwise_scaled_fp8_bs_amd import inputs
 from oracle import quant
 from gpu_support import (bits16, check_canaries, check_scale_canaries, f32bits, guarded, need_gpu,
                          scale_buffer, special_input, u8)
@@ -200,3 +201,55 @@ def test_empty_inputs():
     q = torch.empty((1, 256), dtype=torch.uint8, device="cuda")[:0]
     bs.bs_quant_1x128(x, q, bs.empty_scales(2, 0, "cuda", pad=4))
     torch.cuda.synchronize()
+
+
+def test_quant_large_one_workgroup_per_tile():
+    """Operands of at least 8 persistent grids' worth of tiles (here 8192 tiles
+    against 256 CUs x 3 workgroups) are launched with one workgroup per tile:
+    the 1x128 row + column pass and the 128x128 pass in both layouts must
+    match the oracle bit for bit there too.  Blocks are independent, so the
+    oracle run on a 128x128 tile gives that tile's exact expected bytes; 40
+    seeded tiles are checked, including the first and the last, with planted
+    zero, tiny and saturating tiles among them."""
+    need_gpu()
+    R, C = 8192, 16384
+    x = inputs.bf16_normal((R, C), 1.0, seed=41)
+    rng = np.random.default_rng(41)
+    tr, tc = R // 128, C // 128
+    picks = [(0, 0), (tr - 1, tc - 1)] + [tuple(t) for t in rng.integers(0, [tr, tc], size=(38, 2))]
+    (zr, zc), (yr, yc), (br, bc) = picks[2], picks[3], picks[4]
+    x[zr * 128:(zr + 1) * 128, zc * 128:(zc + 1) * 128] = 0.0
+    x[yr * 128:(yr + 1) * 128, yc * 128:(yc + 1) * 128] *= 1e-20
+    x[br * 128:(br + 1) * 128, bc * 128:(bc + 1) * 128] *= 1e30
+    xg = x.cuda()
+    qr = torch.empty((R, C), dtype=torch.uint8, device="cuda")
+    sr = bs.empty_scales(C // 128, R, "cuda")
+    qc = torch.empty((C, R), dtype=torch.uint8, device="cuda")
+    sc = bs.empty_scales(R // 128, C, "cuda")
+    print(f"quant_1x128 rows+cols, one workgroup per tile, {R}x{C}", flush=True)
+    bs.bs_quant_1x128(xg, qr, sr, qc, sc)
+    qw = torch.empty((R, C), dtype=torch.uint8, device="cuda")
+    sw = bs.empty_scales(C // 128, R // 128, "cuda")
+    qwt = torch.empty((1, C, R), dtype=torch.uint8, device="cuda")
+    swt = bs.empty_scales(R // 128, C // 128, "cuda")[None]
+    print(f"quant_128x128 both layouts, one workgroup per tile, {R}x{C}", flush=True)
+    bs.bs_quant_128x128_both(xg.view(1, R, C), qw, sw, qwt, swt)
+    torch.cuda.synchronize()
+    xb = bits16(x)
+    got = {n: t.cpu().numpy() for n, t in
+           dict(qr=qr, qc=qc, qw=qw, qwt=qwt[0]).items()}
+    gs = {n: t.cpu().numpy().view(np.uint32) for n, t in dict(sr=sr, sc=sc, sw=sw, swt=swt[0]).items()}
+    for (i, j) in picks:
+        rs, cs = slice(i * 128, (i + 1) * 128), slice(j * 128, (j + 1) * 128)
+        t = np.ascontiguousarray(xb[rs, cs])
+        q, s = quant.quant_1x128_rowwise(t)
+        assert np.array_equal(got["qr"][rs, cs], q), f"row codes of tile {(i, j)}"
+        assert np.array_equal(gs["sr"][j, rs], s[:, 0].view(np.uint32)), f"row scales of tile {(i, j)}"
+        q, s = quant.quant_1x128_colwise(t)
+        assert np.array_equal(got["qc"][cs, rs], q), f"column codes of tile {(i, j)}"
+        assert np.array_equal(gs["sc"][i, cs], s[:, 0].view(np.uint32)), f"column scales of tile {(i, j)}"
+        q, s = quant.quant_128x128(t)
+        assert np.array_equal(got["qw"][rs, cs], q), f"128x128 codes of tile {(i, j)}"
+        assert gs["sw"][j, i] == s.view(np.uint32)[0, 0], f"128x128 scale of tile {(i, j)}"
+        assert np.array_equal(got["qwt"][cs, rs], q.T), f"transposed 128x128 codes of tile {(i, j)}"
+        assert gs["swt"][i, j] == s.view(np.uint32)[0, 0], f"transposed 128x128 scale of tile {(i, j)}"
