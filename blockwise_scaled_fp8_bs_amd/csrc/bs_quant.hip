@@ -16,8 +16,8 @@
 // Workgroups are persistent: each walks the tiles with a grid stride and
 // loads the next tile's bf16 data into registers before working on the
 // current one, so HBM reads overlap the arithmetic and no partly filled last
-// wave of workgroups is left (the 1x128 and 128x128 passes over large
-// operands launch one workgroup per tile instead: persistent_blocks).  LDS
+// wave of workgroups is left (passes over large operands launch one
+// workgroup per tile instead: persistent_blocks).  LDS
 // buffers alternate between consecutive tiles, so one barrier per LDS
 // exchange suffices.  Each tile reads HBM once and writes each requested
 // output once.
@@ -648,14 +648,14 @@ __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(Quant128Args a)
 }
 
 // Persistent grid: as many workgroups as fit on the device at once (per the
-// kernel's occupancy), never more than the tiles.  With `tile_per_block`, a
-// problem of at least 8 such grids' worth of tiles launches one workgroup per
-// tile instead (the tile loop then runs once and never prefetches): on the
-// large operands of the FFN and MoE layers the 1x128 and 128x128 passes run
-// 5-12 % faster that way (in-order dispatch keeps the tiles in flight in one
-// contiguous window), while the smaller ones are no faster and stay persistent.
+// kernel's occupancy), never more than the tiles.  A problem of at least 8
+// such grids' worth of tiles launches one workgroup per tile instead (the
+// tile loop then runs once and never prefetches): on the large operands of
+// the FFN and MoE layers every quantizer runs 4-12 % faster that way
+// (in-order dispatch keeps the tiles in flight in one contiguous window),
+// while the dense-size passes are no faster and stay persistent.
 template <typename K>
-int64_t persistent_blocks(K kernel, int64_t tiles, bool tile_per_block = false) {
+int64_t persistent_blocks(K kernel, int64_t tiles) {
     int dev = 0, cus = 256, per_cu = 2;
     if (hipGetDevice(&dev) == hipSuccess) {
         int v = 0;
@@ -664,15 +664,15 @@ int64_t persistent_blocks(K kernel, int64_t tiles, bool tile_per_block = false) 
     int occ = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, 0) == hipSuccess && occ > 0) per_cu = occ;
     const int64_t cap = (int64_t)cus * per_cu;
-    if (tile_per_block && tiles >= 8 * cap) return tiles;
+    if (tiles >= 8 * cap) return tiles;
     return tiles < cap ? tiles : cap;
 }
 
 }  // namespace
 
 template <typename K, typename A>
-hipError_t launch_persistent(K kernel, const A& a, int64_t tiles, hipStream_t stream, bool tile_per_block = false) {
-    dim3 grid((unsigned)persistent_blocks(kernel, tiles, tile_per_block)), block(kThreads);
+hipError_t launch_persistent(K kernel, const A& a, int64_t tiles, hipStream_t stream) {
+    dim3 grid((unsigned)persistent_blocks(kernel, tiles)), block(kThreads);
     hipLaunchKernelGGL(kernel, grid, block, 0, stream, a);
     return hipGetLastError();
 }
@@ -685,9 +685,9 @@ hipError_t launch_quant_1x128(const Quant1x128Args& a, bool row, bool col, bool 
         if (row) return launch_persistent(quant_1x128_kernel<true, false, true>, a, tiles, stream);
         return launch_persistent(quant_1x128_kernel<false, true, true>, a, tiles, stream);
     }
-    if (row && col) return launch_persistent(quant_1x128_kernel<true, true, false>, a, tiles, stream, true);
-    if (row) return launch_persistent(quant_1x128_kernel<true, false, false>, a, tiles, stream, true);
-    return launch_persistent(quant_1x128_kernel<false, true, false>, a, tiles, stream, true);
+    if (row && col) return launch_persistent(quant_1x128_kernel<true, true, false>, a, tiles, stream);
+    if (row) return launch_persistent(quant_1x128_kernel<true, false, false>, a, tiles, stream);
+    return launch_persistent(quant_1x128_kernel<false, true, false>, a, tiles, stream);
 }
 
 hipError_t launch_swiglu_bwd_quant(const SwigluBwdArgs& a, bool row, bool col, hipStream_t stream) {
@@ -709,10 +709,10 @@ hipError_t launch_mx_quant(const MxQuantArgs& a, bool row, bool col, hipStream_t
 hipError_t launch_quant_128x128(const Quant128Args& a, Quant128Mode mode, hipStream_t stream) {
     const int64_t tiles = a.G * a.row_tiles * a.col_tiles;
     if (tiles == 0) return hipSuccess;
-    if (mode == kQ128Both) return launch_persistent(quant_128x128_kernel<kQ128Both>, a, tiles, stream, true);
+    if (mode == kQ128Both) return launch_persistent(quant_128x128_kernel<kQ128Both>, a, tiles, stream);
     if (mode == kQ128Transposed)
-        return launch_persistent(quant_128x128_kernel<kQ128Transposed>, a, tiles, stream, true);
-    return launch_persistent(quant_128x128_kernel<kQ128Rows>, a, tiles, stream, true);
+        return launch_persistent(quant_128x128_kernel<kQ128Transposed>, a, tiles, stream);
+    return launch_persistent(quant_128x128_kernel<kQ128Rows>, a, tiles, stream);
 }
 
 }  // namespace bs

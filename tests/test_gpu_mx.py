@@ -129,16 +129,17 @@ def test_mx_quant_every_scale_exponent():
     _same(u8(sc).T[:C], sc_ref, "column scales")
 
 
-def test_mx_quant_full_size_sampled():
-    # the bench's activation shape; rows and 32-row slabs checked one by one
+@pytest.mark.parametrize("R,C", [(8192, 4096), (8192, 16384)])
+def test_mx_quant_full_size_sampled(R, C):
+    # the bench's activation shape (a persistent grid) and one of 8192 tiles
+    # (one workgroup per tile); rows and 32-row slabs checked one by one
     need_gpu()
-    R, C = 8192, 4096
     x = inputs.bf16_normal((R, C), 1.0, 11, device="cuda")
     q = torch.empty((R, C), dtype=torch.uint8, device="cuda")
     s = bs.empty_mx_scales(C // 32, R, "cuda")
     qc = torch.empty((C, R), dtype=torch.uint8, device="cuda")
     sc = bs.empty_mx_scales(R // 32, C, "cuda")
-    print("mx_quant 8192 x 4096", flush=True)
+    print(f"mx_quant {R} x {C}", flush=True)
     bs.bs_mx_quant_1x32(x, q, s, qc, sc)
     torch.cuda.synchronize()
     rng = np.random.default_rng(3)

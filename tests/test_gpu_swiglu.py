@@ -200,3 +200,76 @@ def test_swiglu_bwd_quant_views_of_a_stacked_activation():
     q_ref, s_ref = quant.quant_1x128_rowwise(_dab_ref(a, b, dh))
     assert np.array_equal(u8(qr), q_ref)
     assert np.array_equal(sr.cpu().numpy().T[:R], s_ref)
+
+
+# ---- operands large enough for one workgroup per tile ----
+
+def _sampled_tiles(R, C, seed, n=24):
+    rng = np.random.default_rng(seed)
+    tr, tc = R // 128, C // 128
+    return [(0, 0), (tr - 1, tc - 1)] + [tuple(int(v) for v in t) for t in rng.integers(0, [tr, tc], size=(n, 2))]
+
+
+def test_swiglu_quant_large_sampled():
+    """8192 x 12288 (6144 tiles, at least 8 persistent grids of this kernel:
+    one workgroup per tile): h and the codes and scales of sampled 128x128
+    tiles bit-exact against the oracle run on those tiles (blocks are
+    independent, so a tile's expected bytes depend on that tile alone)."""
+    need_gpu()
+    R, C = 8192, 12288
+    a, b = _inputs(R, C, seed=71)
+    h = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
+    qr = torch.empty((R, C), dtype=torch.uint8, device="cuda")
+    sr = bs.empty_scales(C // 128, R, "cuda")
+    qc = torch.empty((C, R), dtype=torch.uint8, device="cuda")
+    sc = bs.empty_scales(R // 128, C, "cuda")
+    print(f"swiglu_quant {R}x{C} (one workgroup per tile)", flush=True)
+    bs.bs_swiglu_quant_1x128(a.cuda(), b.cuda(), h, qr, sr, qc, sc)
+    torch.cuda.synchronize()
+    ab, bb = bits16(a), bits16(b)
+    hg, qrg, qcg = bits16(h), u8(qr), u8(qc)
+    srg, scg = sr.cpu().numpy(), sc.cpu().numpy()
+    for (i, j) in _sampled_tiles(R, C, 71):
+        rs, cs = slice(128 * i, 128 * (i + 1)), slice(128 * j, 128 * (j + 1))
+        h_ref = swiglu.swiglu(np.ascontiguousarray(ab[rs, cs]), np.ascontiguousarray(bb[rs, cs]))
+        _assert_same_bits(hg[rs, cs], h_ref, f"h of tile {(i, j)}")
+        q_ref, s_ref = quant.quant_1x128_rowwise(h_ref)
+        assert np.array_equal(qrg[rs, cs], q_ref), f"row codes of tile {(i, j)}"
+        assert np.array_equal(srg[j, rs], s_ref[:, 0]), f"row scales of tile {(i, j)}"
+        q_ref, s_ref = quant.quant_1x128_colwise(h_ref)
+        assert np.array_equal(qcg[cs, rs], q_ref), f"column codes of tile {(i, j)}"
+        assert np.array_equal(scg[i, cs], s_ref[:, 0]), f"column scales of tile {(i, j)}"
+
+
+def test_swiglu_bwd_quant_large_sampled():
+    """The backward at 8192 x 12288 (one workgroup per tile): [da | db] and its
+    codes and scales on sampled tiles bit-exact against the oracle; tile
+    (i, j) of the input feeds tiles (i, j) (da) and (i, j + C/128) (db) of the
+    [R, 2C] output."""
+    need_gpu()
+    R, C = 8192, 12288
+    a, b, dh = _grad_inputs(R, C, seed=73)
+    dab = torch.empty((R, 2 * C), dtype=torch.bfloat16, device="cuda")
+    qr = torch.empty((R, 2 * C), dtype=torch.uint8, device="cuda")
+    sr = bs.empty_scales(2 * C // 128, R, "cuda")
+    qc = torch.empty((2 * C, R), dtype=torch.uint8, device="cuda")
+    sc = bs.empty_scales(R // 128, 2 * C, "cuda")
+    print(f"swiglu_bwd_quant {R}x{C} (one workgroup per tile)", flush=True)
+    bs.bs_swiglu_bwd_quant_1x128(a.cuda(), b.cuda(), dh.cuda(), dab, qr, sr, qc, sc)
+    torch.cuda.synchronize()
+    ab, bb, db_ = bits16(a), bits16(b), bits16(dh)
+    dg, qrg, qcg = bits16(dab), u8(qr), u8(qc)
+    srg, scg = sr.cpu().numpy(), sc.cpu().numpy()
+    for (i, j) in _sampled_tiles(R, C, 73):
+        rs, cs = slice(128 * i, 128 * (i + 1)), slice(128 * j, 128 * (j + 1))
+        da, db = swiglu.swiglu_backward(*(np.ascontiguousarray(t[rs, cs]) for t in (ab, bb, db_)))
+        for part, ref in ((0, da), (1, db)):
+            oc = slice(128 * (j + part * C // 128), 128 * (j + part * C // 128 + 1))
+            jj = j + part * C // 128
+            _assert_same_bits(dg[rs, oc], ref, f"{'db' if part else 'da'} of tile {(i, j)}")
+            q_ref, s_ref = quant.quant_1x128_rowwise(ref)
+            assert np.array_equal(qrg[rs, oc], q_ref), f"row codes of tile {(i, jj)}"
+            assert np.array_equal(srg[jj, rs], s_ref[:, 0]), f"row scales of tile {(i, jj)}"
+            q_ref, s_ref = quant.quant_1x128_colwise(ref)
+            assert np.array_equal(qcg[oc, rs], q_ref), f"column codes of tile {(i, jj)}"
+            assert np.array_equal(scg[i, oc], s_ref[:, 0]), f"column scales of tile {(i, jj)}"
