@@ -664,7 +664,9 @@ int64_t persistent_blocks(K kernel, int64_t tiles) {
     int occ = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, 0) == hipSuccess && occ > 0) per_cu = occ;
     const int64_t cap = (int64_t)cus * per_cu;
-    if (tiles >= 8 * cap) return tiles;
+    // (capped at 2^23 workgroups, 2^31 threads; the grid-stride loop takes the rest)
+    constexpr int64_t kMaxBlocks = (int64_t)1 << 23;
+    if (tiles >= 8 * cap) return tiles < kMaxBlocks ? tiles : kMaxBlocks;
     return tiles < cap ? tiles : cap;
 }
 
