@@ -416,3 +416,27 @@ def test_group_m_many_groups(G):
             assert ok, f"group {g}: worst {worst}"
         start = e
     check_canaries(full, M, N)
+
+
+def test_scaled_mm_largest_leading_dimensions():
+    """Operands stored with leading dimensions just under the 2^22 limit the
+    boundary accepts (1 GiB per operand view): the 32-bit lane and tile
+    offsets of the copies must not wrap."""
+    need_gpu()
+    M, N, K = 256, 256, 512
+    ld = (1 << 22) - 128
+    qa, sa = operand_1x128(M, K, 1.0, seed=91)
+    qb, sb = operand_128x128(N, K, 0.02, seed=92)
+    abuf = torch.zeros((M, ld), dtype=torch.uint8, device="cuda")
+    bbuf = torch.zeros((N, ld), dtype=torch.uint8, device="cuda")
+    a = abuf[:, ld - K:]                 # the operand ends at the last byte of each row
+    b = bbuf[:, ld - K:]
+    a.copy_(torch.from_numpy(qa).cuda())
+    b.copy_(torch.from_numpy(qb).cuda())
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    print(f"scaled_mm lda=ldb={ld}", flush=True)
+    bs.bs_scaled_mm(a, to_gpu_scales(sa), b, to_gpu_scales(sb), bs.BS_SCALE_128X128, out=out)
+    torch.cuda.synchronize()
+    check_result(out, qa, sa, qb, sb, 128)
+    del abuf, bbuf
+    torch.cuda.empty_cache()

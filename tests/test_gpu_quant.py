@@ -253,3 +253,38 @@ def test_quant_large_one_workgroup_per_tile():
         assert gs["sw"][j, i] == s.view(np.uint32)[0, 0], f"128x128 scale of tile {(i, j)}"
         assert np.array_equal(got["qwt"][cs, rs], q.T), f"transposed 128x128 codes of tile {(i, j)}"
         assert gs["swt"][i, j] == s.view(np.uint32)[0, 0], f"transposed 128x128 scale of tile {(i, j)}"
+
+
+def test_quant_largest_leading_dimensions():
+    """x and the row codes stored with leading dimensions just under the 2^22
+    limit the boundary accepts: codes and scales still bit-exact."""
+    need_gpu()
+    R, C = 128, 512
+    ld = (1 << 22) - 64
+    x = special_input(R, C, seed=93)
+    xbuf = torch.zeros((R, ld), dtype=torch.bfloat16, device="cuda")
+    xg = xbuf[:, ld - C:]
+    xg.copy_(x.cuda())
+    qbuf = torch.zeros((R, ld), dtype=torch.uint8, device="cuda")
+    qr = qbuf[:, ld - C:]
+    sr = bs.empty_scales(C // 128, R, "cuda")
+    qc = torch.empty((C, R), dtype=torch.uint8, device="cuda")
+    sc = bs.empty_scales(R // 128, C, "cuda")
+    print(f"quant_1x128 ld_x=ld_qr={ld}", flush=True)
+    bs.bs_quant_1x128(xg, qr, sr, qc, sc)
+    q128 = torch.empty((R, C), dtype=torch.uint8, device="cuda")
+    s128 = bs.empty_scales(C // 128, R // 128, "cuda")
+    bs.bs_quant_128x128(xg, q128, s128)
+    torch.cuda.synchronize()
+    xb = bits16(x)
+    q_ref, s_ref = quant.quant_1x128_rowwise(xb)
+    assert_codes(qr, q_ref)
+    assert_scales(sr, s_ref)
+    q_ref, s_ref = quant.quant_1x128_colwise(xb)
+    assert_codes(qc, q_ref)
+    assert_scales(sc, s_ref)
+    q_ref, s_ref = quant.quant_128x128(xb)
+    assert_codes(q128, q_ref)
+    assert_scales(s128, s_ref)
+    del xbuf, qbuf
+    torch.cuda.empty_cache()
