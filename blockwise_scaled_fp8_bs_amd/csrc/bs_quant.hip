@@ -17,10 +17,9 @@
 // loads the next tile's bf16 data into registers before working on the
 // current one, so HBM reads overlap the arithmetic and no partly filled last
 // wave of workgroups is left (passes over large operands launch one
-// workgroup per tile instead: persistent_blocks).  LDS
-// buffers alternate between consecutive tiles, so one barrier per LDS
-// exchange suffices.  Each tile reads HBM once and writes each requested
-// output once.
+// workgroup per tile instead: persistent_blocks).  LDS buffers alternate
+// between consecutive tiles, so one barrier per LDS exchange suffices.  Each
+// tile reads HBM once and writes each requested output once.
 #include "bs_kernels.h"
 #include "bs_device.h"
 #include "bs_mx.h"
@@ -652,7 +651,8 @@ __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(Quant128Args a)
 // such grids' worth of tiles launches one workgroup per tile instead (the
 // tile loop then runs once and never prefetches): on the large operands of
 // the FFN and MoE layers every quantizer runs 4-12 % faster that way
-// (in-order dispatch keeps the tiles in flight in one contiguous window),
+// (likely because in-order dispatch keeps the tiles in flight within one
+// contiguous window of rows, where persistent workgroups drift apart),
 // while the dense-size passes are no faster and stay persistent.
 template <typename K>
 int64_t persistent_blocks(K kernel, int64_t tiles) {
@@ -712,8 +712,7 @@ hipError_t launch_quant_128x128(const Quant128Args& a, Quant128Mode mode, hipStr
     const int64_t tiles = a.G * a.row_tiles * a.col_tiles;
     if (tiles == 0) return hipSuccess;
     if (mode == kQ128Both) return launch_persistent(quant_128x128_kernel<kQ128Both>, a, tiles, stream);
-    if (mode == kQ128Transposed)
-        return launch_persistent(quant_128x128_kernel<kQ128Transposed>, a, tiles, stream);
+    if (mode == kQ128Transposed) return launch_persistent(quant_128x128_kernel<kQ128Transposed>, a, tiles, stream);
     return launch_persistent(quant_128x128_kernel<kQ128Rows>, a, tiles, stream);
 }
 
