@@ -1,0 +1,52 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU guard and the lookup of
+HBM traffic in the committed rocprofv3 counter summaries."""
+
+import glob
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=300)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
+    assert res.stdout == ""
+
+
+def _traffic_lines():
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*_rocprof.txt")):
+        for line in open(path):
+            if line.startswith("traffic_bytes "):
+                sym = line[len("traffic_bytes "):line.index(" grid=")]
+                fields = line.split()
+                yield path, sym, int(fields[-2]), fields[-1].split("=", 1)[1]
+
+
+def test_counter_traffic_reads_the_dominant_kernel():
+    # the dense workload's dominant kernel is the wgrad GEMM; its summary line
+    # must be found and returned as bytes per launch
+    # (None once the kernel's sources differ from those the counters were taken on)
+    sym = bench.KERNEL_SYMBOL["gemm_wgrad"]
+    want = [(b, h) for p, s, b, h in _traffic_lines()
+            if os.path.basename(p) == "dense_8192x4096x4096_rocprof.txt" and s == sym]
+    assert len(want) == 1
+    got = bench.counter_traffic("dense_8192x4096x4096", "gemm_wgrad")
+    if want[0][1] != bench.kernel_source_hash(sym):
+        assert got is None
+        return
+    assert got == want[0][0]
+    # above the algorithmic bytes (two 32 MiB operands and a 32 MiB output)
+    # and below what no cache reuse at all would move
+    assert 96 << 20 < got < 1 << 30
+
+
+def test_counter_traffic_without_a_summary_is_none():
+    assert bench.counter_traffic("linear_fwd_256x512x256", "gemm_fwd") is None
+    assert bench.counter_traffic("dense_8192x4096x4096", "no_such_kernel") is None
+    assert bench.kernel_source_hash("no_such_kernel<0>") is None
