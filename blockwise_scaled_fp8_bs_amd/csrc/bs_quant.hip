@@ -140,9 +140,10 @@ __device__ __forceinline__ float bf16_from_double(double d) {
 constexpr float kTieWindow = 16.0f;   // fp32 ulps; the fp32 paths err by < 6
 constexpr float kMinNormal = 1.17549435e-38f;  // 2^-126
 
-// The float64 evaluations, out of line: they run for a few elements in a
-// thousand, and one copy keeps the unrolled fp32 paths small.
-__device__ __attribute__((noinline)) float swiglu_bf16_f64(float a, float b) {
+// The float64 evaluations, for the few elements in a thousand the fp32 paths
+// leave undecided; each kernel calls them from one per-lane loop, outside its
+// unrolled fp32 code.
+__device__ __forceinline__ float swiglu_bf16_f64(float a, float b) {
     const double ad = a;
     return bf16_from_double(ad / (1.0 + exp(-ad)) * (double)b);
 }
@@ -155,21 +156,20 @@ __device__ __forceinline__ float2 swiglu_grad_bf16_f64(float a, float b, float d
     return make_float2(bf16_from_double(dd * bd * sd * (1.0 + ad * snd)), bf16_from_double(dd * (ad * sd)));
 }
 
-// h = silu(a) * b rounded once to bf16.  fp32 unless a <= -69 (exp(-a) near
-// fp32 overflow), silu(a) subnormal, or the value near a tie.
-__device__ __forceinline__ float swiglu_bf16(float a, float b) {
-    if (a > -69.0f) {
-        const float silu = a / (1.0f + expf(-a));
-        const float r = silu * b;
-        const bool normal = silu == 0.0f || fabsf(silu) >= kMinNormal;
-        if (normal && __builtin_isfinite(r) && tie_distance(r) > kTieWindow) return (float)(__bf16)r;
-    }
-    return swiglu_bf16_f64(a, b);
-}
-
-// Undecided elements of the gradient come out with da = +inf (bf16 0x7F80),
-// which marks them for the float64 pass (a true +inf is just recomputed).
+// Undecided elements come out as +inf (bf16 0x7F80), which marks them for the
+// float64 pass (the fp32 paths never return a true infinity: it is undecided).
 constexpr uint32_t kRedoBits = 0x7F80u;
+
+// h = silu(a) * b rounded once to bf16, in fp32; +inf (to be redone in
+// float64) where a <= -69 (exp(-a) near fp32 overflow), silu(a) is subnormal,
+// the product is not finite, or it lies near a rounding tie.
+__device__ __forceinline__ float swiglu_fast(float a, float b) {
+    const float silu = a / (1.0f + expf(-a));
+    const float r = silu * b;
+    const bool normal = silu == 0.0f || fabsf(silu) >= kMinNormal;
+    const bool ok = a > -69.0f && normal && __builtin_isfinite(r) && tie_distance(r) > kTieWindow;
+    return ok ? (float)(__bf16)r : __builtin_inff();
+}
 
 // da = dh * b * silu'(a) and db = dh * silu(a), silu'(a) = s (1 + a (1 - s)),
 // s = 1 / (1 + exp(-a)), in fp32, each rounded to bf16; da = +inf where
@@ -359,14 +359,22 @@ __global__ __launch_bounds__(kThreads) void quant_1x128_kernel(Quant1x128Args a)
         const int64_t r0 = (tile / a.col_tiles) * kTile, c0 = (tile % a.col_tiles) * kTile;
         const int64_t rows = (a.R - r0) < kTile ? (a.R - r0) : kTile;
         TileRegs tl;
-        unpack_tile(raw, tl);
+        Raw ph;  // gated form: h packed as bf16, +inf where the fp32 path left it undecided
         if (SWIGLU) {
-            TileRegs ty;
-            unpack_tile(raw_y, ty);
+            // row by row from the packed inputs, so that no float tile is live
+            // while the next tile's inputs are loaded
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < 8; ++i) {
+                float fa[8], fb[8], g[8];
+                unpack8(raw.v[i], fa);
+                unpack8(raw_y.v[i], fb);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) tl.f[i][j] = swiglu_bf16(tl.f[i][j], ty.f[i][j]);
+                for (int j = 0; j < 8; ++j) g[j] = swiglu_fast(fa[j], fb[j]);
+                ph.v[i] = make_uint4(pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3]), pack_bf16(g[4], g[5]),
+                                     pack_bf16(g[6], g[7]));
+            }
+        } else {
+            unpack_tile(raw, tl);
         }
         const int64_t next = tile + gridDim.x;
         if (next < ntiles) {
@@ -375,10 +383,17 @@ __global__ __launch_bounds__(kThreads) void quant_1x128_kernel(Quant1x128Args a)
                 load_raw(a.y, a.ld_y, (next / a.col_tiles) * kTile, (next % a.col_tiles) * kTile, a.R, voff_y,
                          raw_y);
         }
-        if (SWIGLU && a.h != nullptr) {
-            Raw ph;
-            pack_tile(tl, ph);
-            store_raw(ph, a.h + r0 * a.ld_h + c0, a.ld_h, rows, tr, tc);
+        if (SWIGLU) {
+            // undecided elements: their inputs are read again (a few per tile)
+            // and h is recomputed in float64
+            fixup_block(ph, [&](int e) {
+                const int64_t r = r0 + 8 * tr + (e >> 3), c = c0 + 8 * tc + (e & 7);
+                if (r >= a.R) return;  // rows past the end read as zeros and are never marked
+                raw_set(ph, e, swiglu_bf16_f64(__uint_as_float((uint32_t)a.x[r * a.ld_x + c] << 16),
+                                               __uint_as_float((uint32_t)a.y[r * a.ld_y + c] << 16)));
+            });
+            if (a.h != nullptr) store_raw(ph, a.h + r0 * a.ld_h + c0, a.ld_h, rows, tr, tc);
+            unpack_tile(ph, tl);
         }
         if (ROW) quant_tile_rows(tl, rows, a.q_row + r0 * a.ld_qr + c0, a.ld_qr, a.s_row + (c0 / kTile) * a.ld_sr + r0, tr, tc);
         if (COL)
