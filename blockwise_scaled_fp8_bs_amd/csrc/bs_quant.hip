@@ -222,6 +222,26 @@ __device__ __forceinline__ void raw_set(Raw& r, int e, float v) {
     }
 }
 
+// The same replacement with branch-free blends: every word is rewritten with a
+// mask that is zero except at the target half-word, so the block stays in
+// registers (the selects above can be turned into an indexed store, which puts
+// the block in private memory).
+__device__ __forceinline__ void raw_set_blend(Raw& r, int e, float v) {
+    const uint32_t w = (uint32_t)e >> 1;
+    const uint32_t h16 = __float_as_uint(v) >> 16;
+    const uint32_t field = (e & 1) ? 0xFFFF0000u : 0x0000FFFFu;
+    const uint32_t put = (e & 1) ? (h16 << 16) : h16;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t mx = (4u * i + 0u == w) ? field : 0u, my = (4u * i + 1u == w) ? field : 0u;
+        const uint32_t mz = (4u * i + 2u == w) ? field : 0u, mw = (4u * i + 3u == w) ? field : 0u;
+        r.v[i].x = (r.v[i].x & ~mx) | (put & mx);
+        r.v[i].y = (r.v[i].y & ~my) | (put & my);
+        r.v[i].z = (r.v[i].z & ~mz) | (put & mz);
+        r.v[i].w = (r.v[i].w & ~mw) | (put & mw);
+    }
+}
+
 // Re-evaluates, in float64, the elements of a thread's packed block that the
 // fp32 path marked (+inf); fn(e) does element e.  The marks are found with
 // integer arithmetic only (per-element compares would keep 64 lane masks
@@ -389,8 +409,8 @@ __global__ __launch_bounds__(kThreads) void quant_1x128_kernel(Quant1x128Args a)
             fixup_block(ph, [&](int e) {
                 const int64_t r = r0 + 8 * tr + (e >> 3), c = c0 + 8 * tc + (e & 7);
                 if (r >= a.R) return;  // rows past the end read as zeros and are never marked
-                raw_set(ph, e, swiglu_bf16_f64(__uint_as_float((uint32_t)a.x[r * a.ld_x + c] << 16),
-                                               __uint_as_float((uint32_t)a.y[r * a.ld_y + c] << 16)));
+                raw_set_blend(ph, e, swiglu_bf16_f64(__uint_as_float((uint32_t)a.x[r * a.ld_x + c] << 16),
+                                                     __uint_as_float((uint32_t)a.y[r * a.ld_y + c] << 16)));
             });
             if (a.h != nullptr) store_raw(ph, a.h + r0 * a.ld_h + c0, a.ld_h, rows, tr, tc);
             unpack_tile(ph, tl);
