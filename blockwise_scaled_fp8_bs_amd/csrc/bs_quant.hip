@@ -478,8 +478,8 @@ __global__ __launch_bounds__(kThreads) void swiglu_bwd_quant_kernel(SwigluBwdArg
             const float2 g = swiglu_grad_bf16_f64(__uint_as_float((uint32_t)a.a[r * a.ld_a + c] << 16),
                                                   __uint_as_float((uint32_t)a.b[r * a.ld_b + c] << 16),
                                                   __uint_as_float((uint32_t)a.dh[r * a.ld_dh + c] << 16));
-            raw_set(pda, e, g.x);
-            raw_set(pdb, e, g.y);
+            raw_set_blend(pda, e, g.x);
+            raw_set_blend(pdb, e, g.y);
         });
         if (a.dab != nullptr) {
             store_raw(pda, a.dab + r0 * a.ld_dab + c0, a.ld_dab, rows, tr, tc);
