@@ -207,26 +207,11 @@ __device__ __forceinline__ uint32_t raw_word(const Raw& r, int k) {
 }
 
 // Replaces element e (per lane: row e / 8, column e % 8) of a packed block by
-// a bf16-exact value: selects over the 32 words (rare path).
+// a bf16-exact value (rare path).  Branch-free blends: every word is rewritten
+// with a mask that is zero except at the target half-word, so the block stays
+// in registers (per-word conditional stores can be turned into an indexed
+// store, which puts the block in private memory).
 __device__ __forceinline__ void raw_set(Raw& r, int e, float v) {
-    const int w = e >> 1;
-    const uint32_t h16 = __float_as_uint(v) >> 16;
-    const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-    const uint32_t put = (e & 1) ? (h16 << 16) : h16;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        if (4 * i + 0 == w) r.v[i].x = (r.v[i].x & keep) | put;
-        if (4 * i + 1 == w) r.v[i].y = (r.v[i].y & keep) | put;
-        if (4 * i + 2 == w) r.v[i].z = (r.v[i].z & keep) | put;
-        if (4 * i + 3 == w) r.v[i].w = (r.v[i].w & keep) | put;
-    }
-}
-
-// The same replacement with branch-free blends: every word is rewritten with a
-// mask that is zero except at the target half-word, so the block stays in
-// registers (the selects above can be turned into an indexed store, which puts
-// the block in private memory).
-__device__ __forceinline__ void raw_set_blend(Raw& r, int e, float v) {
     const uint32_t w = (uint32_t)e >> 1;
     const uint32_t h16 = __float_as_uint(v) >> 16;
     const uint32_t field = (e & 1) ? 0xFFFF0000u : 0x0000FFFFu;
@@ -409,7 +394,7 @@ __global__ __launch_bounds__(kThreads) void quant_1x128_kernel(Quant1x128Args a)
             fixup_block(ph, [&](int e) {
                 const int64_t r = r0 + 8 * tr + (e >> 3), c = c0 + 8 * tc + (e & 7);
                 if (r >= a.R) return;  // rows past the end read as zeros and are never marked
-                raw_set_blend(ph, e, swiglu_bf16_f64(__uint_as_float((uint32_t)a.x[r * a.ld_x + c] << 16),
+                raw_set(ph, e, swiglu_bf16_f64(__uint_as_float((uint32_t)a.x[r * a.ld_x + c] << 16),
                                                      __uint_as_float((uint32_t)a.y[r * a.ld_y + c] << 16)));
             });
             if (a.h != nullptr) store_raw(ph, a.h + r0 * a.ld_h + c0, a.ld_h, rows, tr, tc);
@@ -478,8 +463,8 @@ __global__ __launch_bounds__(kThreads) void swiglu_bwd_quant_kernel(SwigluBwdArg
             const float2 g = swiglu_grad_bf16_f64(__uint_as_float((uint32_t)a.a[r * a.ld_a + c] << 16),
                                                   __uint_as_float((uint32_t)a.b[r * a.ld_b + c] << 16),
                                                   __uint_as_float((uint32_t)a.dh[r * a.ld_dh + c] << 16));
-            raw_set_blend(pda, e, g.x);
-            raw_set_blend(pdb, e, g.y);
+            raw_set(pda, e, g.x);
+            raw_set(pdb, e, g.y);
         });
         if (a.dab != nullptr) {
             store_raw(pda, a.dab + r0 * a.ld_dab + c0, a.ld_dab, rows, tr, tc);
