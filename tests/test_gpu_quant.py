@@ -204,7 +204,7 @@ def test_empty_inputs():
 
 
 def test_quant_large_one_workgroup_per_tile():
-    """Operands of at least 8 persistent grids' worth of tiles (here 8192 tiles
+    """Operands of at least 2 persistent grids' worth of tiles (here 8192 tiles
     against 256 CUs x 3 workgroups) are launched with one workgroup per tile:
     the 1x128 row + column pass and the 128x128 pass in both layouts must
     match the oracle bit for bit there too.  Blocks are independent, so the

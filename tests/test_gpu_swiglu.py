@@ -211,7 +211,7 @@ def _sampled_tiles(R, C, seed, n=24):
 
 
 def test_swiglu_quant_large_sampled():
-    """8192 x 12288 (6144 tiles, at least 8 persistent grids of this kernel:
+    """8192 x 12288 (6144 tiles, at least 2 persistent grids of this kernel:
     one workgroup per tile): h and the codes and scales of sampled 128x128
     tiles bit-exact against the oracle run on those tiles (blocks are
     independent, so a tile's expected bytes depend on that tile alone)."""
