@@ -54,13 +54,19 @@ def round_to_bf16(v):
     return bits.astype(np.uint16)
 
 
-def swiglu(a_bits, b_bits):
-    """h = silu(a) * b for bf16 inputs (uint16 bit patterns), as bf16 bits."""
+def swiglu_f64(a_bits, b_bits):
+    """h = silu(a) * b for bf16 inputs (uint16 bit patterns) in float64, before
+    its one rounding to bf16."""
     a = bf16_bits_to_f32(np.asarray(a_bits, dtype=np.uint16)).astype(np.float64)
     b = bf16_bits_to_f32(np.asarray(b_bits, dtype=np.uint16)).astype(np.float64)
     with np.errstate(over="ignore"):
         silu = a / (1.0 + np.exp(-a))          # exp overflow -> inf -> silu = -0
-    return round_to_bf16(silu * b)
+    return silu * b
+
+
+def swiglu(a_bits, b_bits):
+    """h = silu(a) * b for bf16 inputs (uint16 bit patterns), as bf16 bits."""
+    return round_to_bf16(swiglu_f64(a_bits, b_bits))
 
 
 def swiglu_backward(a_bits, b_bits, dh_bits):

@@ -273,3 +273,54 @@ def test_swiglu_bwd_quant_large_sampled():
             q_ref, s_ref = quant.quant_1x128_colwise(ref)
             assert np.array_equal(qcg[oc, rs], q_ref), f"column codes of tile {(i, jj)}"
             assert np.array_equal(scg[i, oc], s_ref[:, 0]), f"column scales of tile {(i, jj)}"
+
+
+@pytest.mark.parametrize("b_kind", ["ones", "threes", "normal"])
+def test_swiglu_quant_every_bf16_gate_value(b_kind):
+    """Every finite bf16 value of a (non-finite patterns replaced by 0) against
+    b = 1, b = 3 and seeded normal b: h bit-exact against the oracle's float64
+    formula rounded once, and the row codes against its quantization of h.
+    Covers the whole range of the fp32 path (its reciprocal, the tie window,
+    the a <= -69 and subnormal hand-offs to float64) value by value."""
+    need_gpu()
+    R, C = 512, 128
+    ab = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ab[(ab & 0x7F80) == 0x7F80] = 0                     # inf / NaN patterns
+    ab = ab.reshape(R, C)
+    if b_kind == "normal":
+        b = inputs.bf16_normal((R, C), 1.0, 77)
+    else:
+        b = torch.full((R, C), 1.0 if b_kind == "ones" else 3.0, dtype=torch.bfloat16)
+    a = _from_bits(ab)
+    h = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
+    qr = torch.empty((R, C), dtype=torch.uint8, device="cuda")
+    sr = bs.empty_scales(C // 128, R, "cuda")
+    print(f"swiglu_quant every bf16 a, b={b_kind}", flush=True)
+    bs.bs_swiglu_quant_1x128(a.cuda(), b.cuda(), h, qr, sr)
+    torch.cuda.synchronize()
+    h_ref = swiglu.swiglu(ab, bits16(b))
+    got = bits16(h)
+    # Where the float64 value is within 2^-48 (relative) of a bf16 tie, float64
+    # cannot tell the side (the last bit of exp decides it), and either
+    # neighbour is the reading's answer, as in the oracle's own pin; there
+    # only, the other neighbour (same sign, one step away) is accepted.
+    diff = got != h_ref
+    if diff.any():
+        v = np.abs(swiglu.swiglu_f64(ab, bits16(b))[diff])
+        _, e = np.frexp(v)                                  # v = m 2^e, m in [0.5, 1)
+        step = np.ldexp(1.0, np.maximum(e - 1 - 7, -133))   # bf16 spacing in v's binade
+        k = v / step
+        near_tie = np.abs(k - np.floor(k) - 0.5) * step < v * 2.0 ** -48
+        one_step = ((got[diff] ^ h_ref[diff]) & 0x8000 == 0) & \
+                   (np.abs(got[diff].astype(np.int32) - h_ref[diff].astype(np.int32)) == 1)
+        bad = ~(near_tie & one_step)
+        assert not bad.any(), f"h: {bad.sum()} elements differ outside the float64 tie region, first at " \
+                              f"{np.argwhere(diff)[np.flatnonzero(bad)[:3]]}"
+    # codes: rows whose h is finite (|a| near the bf16 maximum times |b| > 1
+    # overflows, and infinite values are outside the quantizer's domain) and
+    # equal to the oracle's
+    ok = ((h_ref & 0x7F80) != 0x7F80).all(axis=1) & ~diff.any(axis=1)
+    assert ok.sum() >= R - 8
+    q_ref, s_ref = quant.quant_1x128_rowwise(np.ascontiguousarray(h_ref[ok]))
+    assert np.array_equal(u8(qr)[ok], q_ref)
+    assert np.array_equal(sr.cpu().numpy().T[:R][ok], s_ref)
