@@ -69,9 +69,9 @@ def swiglu(a_bits, b_bits):
     return round_to_bf16(swiglu_f64(a_bits, b_bits))
 
 
-def swiglu_backward(a_bits, b_bits, dh_bits):
+def swiglu_backward_f64(a_bits, b_bits, dh_bits):
     """(da, db) of h = silu(a) * b for bf16 a, b and upstream gradient dh
-    (uint16 bit patterns), each rounded once to bf16 bits."""
+    (uint16 bit patterns) in float64, before their one rounding to bf16."""
     a = bf16_bits_to_f32(np.asarray(a_bits, dtype=np.uint16)).astype(np.float64)
     b = bf16_bits_to_f32(np.asarray(b_bits, dtype=np.uint16)).astype(np.float64)
     dh = bf16_bits_to_f32(np.asarray(dh_bits, dtype=np.uint16)).astype(np.float64)
@@ -81,4 +81,11 @@ def swiglu_backward(a_bits, b_bits, dh_bits):
     silu = a * s
     da = dh * b * s * (1.0 + a * sn)
     db = dh * silu
+    return da, db
+
+
+def swiglu_backward(a_bits, b_bits, dh_bits):
+    """(da, db) of h = silu(a) * b for bf16 a, b and upstream gradient dh
+    (uint16 bit patterns), each rounded once to bf16 bits."""
+    da, db = swiglu_backward_f64(a_bits, b_bits, dh_bits)
     return round_to_bf16(da), round_to_bf16(db)

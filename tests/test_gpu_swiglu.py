@@ -324,3 +324,60 @@ def test_swiglu_quant_every_bf16_gate_value(b_kind):
     q_ref, s_ref = quant.quant_1x128_rowwise(np.ascontiguousarray(h_ref[ok]))
     assert np.array_equal(u8(qr)[ok], q_ref)
     assert np.array_equal(sr.cpu().numpy().T[:R][ok], s_ref)
+
+
+def _tie_tolerant(got, want, v):
+    """Positions where got != want are allowed only where the float64 value v
+    is within 2^-48 (relative) of a bf16 tie and got is the other neighbour."""
+    diff = got != want
+    if not diff.any():
+        return diff
+    x = np.abs(v[diff])
+    _, e = np.frexp(x)
+    step = np.ldexp(1.0, np.maximum(e - 8, -133))
+    k = x / step
+    near_tie = np.abs(k - np.floor(k) - 0.5) * step < x * 2.0 ** -48
+    one_step = ((got[diff] ^ want[diff]) & 0x8000 == 0) & \
+               (np.abs(got[diff].astype(np.int32) - want[diff].astype(np.int32)) == 1)
+    bad = ~(near_tie & one_step)
+    assert not bad.any(), f"{bad.sum()} elements differ outside the float64 tie region, first at " \
+                          f"{np.argwhere(diff)[np.flatnonzero(bad)[:3]]}"
+    return diff
+
+
+@pytest.mark.parametrize("kind", ["unit", "normal"])
+def test_swiglu_bwd_every_bf16_gate_value(kind):
+    """The backward on every finite bf16 value of a (non-finite patterns
+    replaced by 0): b = 3, dh = 1 and seeded normal b, dh.  [da | db]
+    bit-exact against the oracle (the other neighbour accepted only within
+    2^-48 of a tie, R20), so every branch of the fp32 path and its windows
+    is exercised value by value."""
+    need_gpu()
+    R, C = 512, 128
+    ab = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ab[(ab & 0x7F80) == 0x7F80] = 0
+    ab = ab.reshape(R, C)
+    if kind == "unit":
+        b = torch.full((R, C), 3.0, dtype=torch.bfloat16)
+        dh = torch.full((R, C), 1.0, dtype=torch.bfloat16)
+    else:
+        b = inputs.bf16_normal((R, C), 1.0, 78)
+        dh = inputs.bf16_normal((R, C), 0.01, 79)
+    a = _from_bits(ab)
+    dab = torch.empty((R, 2 * C), dtype=torch.bfloat16, device="cuda")
+    qr = torch.empty((R, 2 * C), dtype=torch.uint8, device="cuda")
+    sr = bs.empty_scales(2 * C // 128, R, "cuda")
+    print(f"swiglu_bwd every bf16 a, {kind}", flush=True)
+    bs.bs_swiglu_bwd_quant_1x128(a.cuda(), b.cuda(), dh.cuda(), dab, qr, sr)
+    torch.cuda.synchronize()
+    da, db = swiglu.swiglu_backward(ab, bits16(b), bits16(dh))
+    g = bits16(dab)
+    va, vb = swiglu.swiglu_backward_f64(ab, bits16(b), bits16(dh))
+    diff_a = _tie_tolerant(g[:, :C], da, va)
+    diff_b = _tie_tolerant(g[:, C:], db, vb)
+    ok = ((da & 0x7F80) != 0x7F80).all(axis=1) & ((db & 0x7F80) != 0x7F80).all(axis=1) & \
+        ~diff_a.any(axis=1) & ~diff_b.any(axis=1)
+    assert ok.sum() >= R - 8
+    q_ref, s_ref = quant.quant_1x128_rowwise(np.ascontiguousarray(np.concatenate([da, db], axis=1)[ok]))
+    assert np.array_equal(u8(qr)[ok], q_ref)
+    assert np.array_equal(sr.cpu().numpy().T[:R][ok], s_ref)
