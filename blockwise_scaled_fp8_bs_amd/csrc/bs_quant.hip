@@ -180,10 +180,12 @@ __device__ __forceinline__ float swiglu_fast(float a, float b) {
 // an intermediate outside the normal range, or a value near a tie).  1 - s is
 // taken as 1 / (1 + exp(a)); near silu'(a) = 0 the sum t = 1 + a (1 - s)
 // cancels, so da's window adds 8 |a (1 - s)| / |t| ulps (infinite at t = 0),
-// written without a division.
+// written without a division.  Both reciprocals are the hardware's (1 ulp;
+// their arguments are >= 1, never subnormal): half an ulp more than a
+// correctly rounded division, inside both windows' margins.
 __device__ __forceinline__ void swiglu_grad_fast(float a, float b, float dh, float& da, float& db) {
-    const float s = 1.0f / (1.0f + expf(-a));
-    const float sn = 1.0f / (1.0f + expf(a));
+    const float s = __builtin_amdgcn_rcpf(1.0f + expf(-a));
+    const float sn = __builtin_amdgcn_rcpf(1.0f + expf(a));
     const float t = __builtin_fmaf(a, sn, 1.0f);
     const float p1 = dh * b, p2 = p1 * s;
     const float rda = p2 * t;
