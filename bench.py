@@ -1,7 +1,8 @@
 """Benchmark of the blockwise-scaled FP8 training hot path on one MI355X.
 
 One step = every kernel of one blockwise-FP8 linear layer's training pass
-over one batch of seeded synthetic data already resident in HBM:
+over one batch of seeded synthetic data already resident in HBM (by default
+the MoE layer: 128000 tokens over 8 experts, K 5120, N 8192):
 
   quantize A [M, K] rows + transposed columns (1x128),
   quantize W [N, K] (128x128) and W^T (3-D colwise layout) in one pass,
@@ -20,6 +21,11 @@ average duration gives `roofline`).  The per-kernel breakdown comes from a
 separate pass of `steps` steps with events around every kernel (events
 between kernels cost GPU time of their own).  The CPU oracle is timed on a
 bounded sample of the same workload on the host (rank 0, N = 1).
+
+The line also carries: the SHA-256 of the bf16 inputs (the bytes both the
+GPU and the oracle consume), the shader and memory clocks sampled while the
+timed steps ran, and a short record of each dense workload (forward, dgrad
+and wgrad of one linear layer) timed the same way.
 """
 
 import argparse
@@ -38,7 +44,8 @@ from blockwise_scaled_fp8_bs_amd import inputs  # noqa: E402
 
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA (no sparsity)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
-DEFAULT_WORKLOAD = "dense_8192x4096x4096"
+DEFAULT_WORKLOAD = "moe_128000x5120x8192_g8"
+EXTRA_WORKLOADS = "dense_8192x4096x4096,ffn_up_16384x5120x8192,ffn_down_16384x7168x2048"
 
 
 def r4(n):
@@ -106,10 +113,15 @@ def counter_traffic(workload, kernel):
 class Step:
     """Buffers and launches of one training step of one workload."""
 
-    def __init__(self, w: inputs.Workload, seed=0, device="cuda"):
+    def __init__(self, w: inputs.Workload, seed=0, device="cuda", scale_pad=0):
+        """``scale_pad`` widens every scale tensor's row stride past
+        roundup4(count) by that many floats (a multiple of 4; the padding is
+        never written)."""
         self.w = w
         M, K, N, G = w.M, w.K, w.N, w.G
         dev = device
+        self.scale_pad = scale_pad
+        r4 = lambda n: (n + 3) // 4 * 4 + scale_pad  # noqa: E731
         a, wt, gout, ends = inputs.make_operands(w, seed=seed, device=dev)
         self.a, self.wt, self.gout = a, wt, gout
         self.grouped = G > 1
@@ -180,7 +192,7 @@ class Step:
         return ks
 
 
-def cpu_oracle_sample(w: inputs.Workload, rows=512, seed=0):
+def cpu_oracle_sample(w: inputs.Workload, rows=2048, seed=0):
     """Time the CPU oracle on a bounded sample of the workload.
 
     The sample is the first `rows` tokens of the same seeded inputs (a
@@ -321,21 +333,181 @@ def mx_grouped_timing(median_ms, seed, which=None):
     return rows
 
 
+def input_digest(step):
+    """SHA-256 of the bf16 inputs of a step (the exact bytes that both the
+    GPU kernels and the CPU oracle consume) and of the group ends."""
+    import hashlib
+    out = {}
+    for name, t in (("A", step.a), ("W", step.wt), ("grad_out", step.gout)):
+        h = hashlib.sha256()
+        h.update(t.contiguous().view(torch.int16).cpu().numpy())
+        out[name] = h.hexdigest()
+    if step.grouped:
+        out["group_end"] = hashlib.sha256(step.ends.cpu().numpy().tobytes()).hexdigest()
+    return out
+
+
+class ClockSampler:
+    """Shader (GFX) and memory (UCLK) clocks of the GPU, read from the driver
+    through amdsmi in a background thread while timed work runs.  Records
+    nothing (and says why) where the driver interface is not available."""
+
+    def __init__(self, interval_s=0.005):
+        import threading
+        self.interval = interval_s
+        self.samples = []
+        self.error = None
+        self.handle = None
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            self.smi = amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            props = torch.cuda.get_device_properties(torch.cuda.current_device())
+            want = (props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
+            for h in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)          # "dddd:bb:dd.f"
+                dom, bus, rest = bdf.split(":")
+                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                    self.handle = h
+            if self.handle is None and len(handles) == 1:
+                self.handle = handles[0]
+            if self.handle is None:
+                self.error = f"no amdsmi handle matches PCI {want}"
+        except Exception as e:  # driver interface missing or not permitted
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _read(self):
+        m = self.smi.amdsmi_get_gpu_metrics_info(self.handle)
+        xcd = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
+        g = sum(xcd) / len(xcd) if xcd else m.get("current_gfxclk")
+        u = m.get("current_uclk")
+        return (float(g) if isinstance(g, (int, float)) else None,
+                float(u) if isinstance(u, (int, float)) else None)
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception as e:
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.interval)
+
+    def start(self):
+        import threading
+        if self.handle is None:
+            return
+        self._stop.clear()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+            self._thread = None
+
+    def summary(self):
+        import statistics
+        g = [s[0] for s in self.samples if s[0]]
+        u = [s[1] for s in self.samples if s[1]]
+        if not g:
+            return {"sclk_mhz": None, "mclk_mhz": None, "samples": 0, "error": self.error,
+                    "source": "amdsmi gpu metrics (current_gfxclks averaged over XCDs, current_uclk)"}
+        return {"sclk_mhz": round(statistics.median(g)), "sclk_min_mhz": round(min(g)),
+                "sclk_max_mhz": round(max(g)), "mclk_mhz": round(statistics.median(u)) if u else None,
+                "samples": len(g), "source": "amdsmi gpu metrics (current_gfxclks averaged over XCDs, "
+                                             "current_uclk), sampled every 5 ms during the timed steps"}
+
+
+def time_step(step, steps, warmup, stream, clocks=None):
+    """Warm up, then (pass 1) time every kernel of `steps` steps with HIP
+    events around each, and (pass 2) time exactly `steps` steps with events
+    around the dominant kernel only.  Returns (per_kernel, dominant name,
+    dominant kernel's average ms in pass 2, wall ms per step of pass 2)."""
+    ks = step.kernels()
+
+    def run_step(events=None, only=None):
+        for i, (_, fn, _, _) in enumerate(ks):
+            timed = events is not None and (only is None or i == only)
+            if timed:
+                events[0 if only is not None else i][0].record(stream)
+            fn()
+            if timed:
+                events[0 if only is not None else i][1].record(stream)
+
+    for _ in range(warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in ks]
+          for _ in range(steps)]
+    for s in range(steps):
+        run_step(ev[s])
+    torch.cuda.synchronize()
+    per_kernel = {}
+    for i, (name, _, work, unit) in enumerate(ks):
+        ms = sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)) / steps
+        rate = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+        peak = FP8_PEAK_TFLOPS if unit == "TFLOP/s" else HBM_PEAK_GBS
+        per_kernel[name] = {"ms": round(ms, 4), "rate": round(rate, 1), "unit": unit,
+                            "frac": round(rate / peak, 4), "work": work}
+    dom_i = max(range(len(ks)), key=lambda i: per_kernel[ks[i][0]]["ms"])
+
+    ev_dom = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]]
+              for _ in range(steps)]
+    torch.cuda.synchronize()
+    if clocks is not None:
+        clocks.start()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        run_step(ev_dom[s], only=dom_i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if clocks is not None:
+        clocks.stop()
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    dom_ms = sum(e[0][0].elapsed_time(e[0][1]) for e in ev_dom) / steps
+    return per_kernel, ks[dom_i][0], dom_ms, ms_per_step
+
+
+def summarize(w, per_kernel, ms_per_step):
+    gemm_flops = 3 * 2.0 * w.M * w.N * w.K
+    gemm_ms = sum(v["ms"] for v in per_kernel.values() if v["unit"] == "TFLOP/s")
+    quant_ms = sum(v["ms"] for v in per_kernel.values() if v["unit"] == "GB/s")
+    quant_bytes = sum(v["work"] for v in per_kernel.values() if v["unit"] == "GB/s")
+    return {
+        "value": gemm_flops / (ms_per_step * 1e-3) / 1e12,
+        "gemm_tflops": gemm_flops / (gemm_ms * 1e-3) / 1e12,
+        "quant_gbs": quant_bytes / (quant_ms * 1e-3) / 1e9,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(inputs.WORKLOADS))
+    ap.add_argument("--extra-workloads", default=EXTRA_WORKLOADS,
+                    help="comma-separated dense workloads timed after the main one and reported per config "
+                         "('' for none)")
+    ap.add_argument("--scale-pad", type=int, default=0,
+                    help="floats of padding past roundup4(count) in every scale tensor's row stride")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-digest", action="store_true", help="skip the SHA-256 of the inputs")
     ap.add_argument("--no-ffn-module", action="store_true", help="skip the gated FFN module timing")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 grouped GEMM timings")
     ap.add_argument("--mx-shapes", default=None,
                     help="comma-separated indices into the MXFP8 shape list (default: all)")
     ap.add_argument("--no-fusion", action="store_true",
                     help="skip the fused gated-activation timings (keeps per-kernel profiles to the step's shapes)")
-    ap.add_argument("--cpu-rows", type=int, default=8192,
+    ap.add_argument("--no-cold", action="store_true", help="skip the copy reference and the cold-cache quantizers")
+    ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="tokens of the workload the CPU oracle baseline runs on (capped at M)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before the workload, run a plain device copy of this many MiB three times "
@@ -354,6 +526,11 @@ def main():
     if w.fwd_only:
         print("the forward-only workload is a parity case, not a bench line", file=sys.stderr)
         sys.exit(2)
+    extras = [x for x in args.extra_workloads.split(",") if x and x != w.name]
+    for x in extras:
+        if x not in inputs.WORKLOADS or inputs.WORKLOADS[x].fwd_only:
+            print(f"unknown or forward-only extra workload {x}", file=sys.stderr)
+            sys.exit(2)
     torch.manual_seed(args.seed)
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20)
@@ -363,59 +540,13 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    step = Step(w, seed=args.seed)
-    ks = step.kernels()
     stream = torch.cuda.current_stream()
+    clocks = ClockSampler()
 
-    def run_step(events=None, only=None):
-        for i, (_, fn, _, _) in enumerate(ks):
-            timed = events is not None and (only is None or i == only)
-            if timed:
-                events[0 if only is not None else i][0].record(stream)
-            fn()
-            if timed:
-                events[0 if only is not None else i][1].record(stream)
-
-    for _ in range(args.warmup):
-        run_step()
-    torch.cuda.synchronize()
-
-    # Pass 1, per-kernel breakdown: HIP events around every kernel of each
-    # step.  (Events between kernels cost GPU time of their own, so this pass
-    # is not the one the step time comes from.)
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in ks]
-          for _ in range(args.steps)]
-    for s in range(args.steps):
-        run_step(ev[s])
-    torch.cuda.synchronize()
-    per_kernel = {}
-    for i, (name, _, work, unit) in enumerate(ks):
-        ms = sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)) / args.steps
-        rate = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
-        peak = FP8_PEAK_TFLOPS if unit == "TFLOP/s" else HBM_PEAK_GBS
-        per_kernel[name] = {"ms": round(ms, 4), "rate": round(rate, 1), "unit": unit,
-                            "frac": round(rate / peak, 4), "work": work}
-    dom_i = max(range(len(ks)), key=lambda i: per_kernel[ks[i][0]]["ms"])
-    dom = ks[dom_i][0]
-
-    # Pass 2, the timed region: exactly `steps` steps, with HIP events only
-    # around the dominant kernel (its live duration gives the roofline).
-    ev_dom = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]]
-              for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        run_step(ev_dom[s], only=dom_i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    dom_ms = sum(e[0][0].elapsed_time(e[0][1]) for e in ev_dom) / args.steps
-
-    gemm_flops = 3 * 2.0 * w.M * w.N * w.K
-    value = gemm_flops / (ms_per_step * 1e-3) / 1e12
-    gemm_ms = sum(v["ms"] for v in per_kernel.values() if v["unit"] == "TFLOP/s")
-    quant_ms = sum(v["ms"] for v in per_kernel.values() if v["unit"] == "GB/s")
-    quant_bytes = sum(v["work"] for v in per_kernel.values() if v["unit"] == "GB/s")
+    step = Step(w, seed=args.seed, scale_pad=args.scale_pad)
+    ks = step.kernels()
+    per_kernel, dom, dom_ms, ms_per_step = time_step(step, args.steps, args.warmup, stream, clocks)
+    summ = summarize(w, per_kernel, ms_per_step)
     d = per_kernel[dom]
     dom_rate = d["work"] / (dom_ms * 1e-3) / (1e12 if d["unit"] == "TFLOP/s" else 1e9)
     dom_peak = FP8_PEAK_TFLOPS if d["unit"] == "TFLOP/s" else HBM_PEAK_GBS
@@ -428,63 +559,15 @@ def main():
         "frac": round(dom_rate / dom_peak, 4),
         "traffic": counter_traffic(w.name, dom),
         "avg_ms": round(dom_ms, 4),
+        "work_per_launch": d["work"],
     }
     for v in per_kernel.values():
         v.pop("work")
-
-    # Practical HBM reference: a plain device copy of 1 GiB (torch copy_),
-    # timed the same way.  The fractions above use the published 8 TB/s peak.
-    n_copy = 1 << 30
-    src = torch.empty(n_copy, dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(2):
-        dst.copy_(src)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(5):
-        dst.copy_(src)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = 2 * n_copy * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-
-    # Quantizers on cold caches: before each timed call, reading the 1 GiB
-    # scratch buffer evicts the inputs from L2 and the 256 MB last-level
-    # cache, so the rate is the HBM-bound one (median of 5).  The flush reads
-    # rather than writes: a written flush leaves the caches full of dirty
-    # lines, and writing those back would be charged to the quantizer (it
-    # cuts the measured rate by a third).  Inside the step above they may
-    # find part of their input still cached.
-    flush_src = src.view(torch.int32)
-    flush_sink = torch.empty((), dtype=torch.int64, device="cuda")
-    cold = {}
-    for name, fn, work, unit in ks:
-        if unit != "GB/s":
-            continue
-        times = []
-        for r in range(5):
-            torch.sum(flush_src, dim=(0,), dtype=torch.int64, out=flush_sink)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
-        ms = sorted(times)[len(times) // 2]
-        rate = work / (ms * 1e-3) / 1e9
-        cold[name] = {"ms": round(ms, 4), "rate": round(rate, 1), "unit": "GB/s", "frac": round(rate / HBM_PEAK_GBS, 4),
-                      "work": work}
-    cold_gbs = sum(v["work"] for v in cold.values()) / (sum(v["ms"] for v in cold.values()) * 1e-3) / 1e9
-    for v in cold.values():
-        v.pop("work")
-    del src, dst
-
-    # Fusion next to the path: the FFN's gated activation h = silu(a) * b
-    # quantized for the next layer (rows + transposed columns), fused in one
-    # kernel versus torch's silu and mul followed by the quantizer.  a, b are
-    # [M, N] bf16 (here the step's output and grad_out buffers stand in).
-    fa, fb = step.out, step.gout
-    M_, N_ = fa.shape
-    fusion = fusion_bwd = None
+    digest = None if args.no_digest else input_digest(step)
+    if step.grouped:
+        cfg_groups = step.group_sizes
+    else:
+        cfg_groups = None
 
     def median_ms(fn, n=7):
         fn()
@@ -498,53 +581,123 @@ def main():
             times.append(e0.elapsed_time(e1))
         return sorted(times)[n // 2]
 
-    if not args.no_fusion:
-        def fused():
-            bs.bs_swiglu_quant_1x128(fa, fb, None, step.qg, step.sg, step.qgT, step.sgT)
+    copy_gbs = cold_gbs = None
+    cold = {}
+    if not args.no_cold:
+        # Practical HBM reference: a plain device copy of 1 GiB (torch copy_),
+        # timed the same way.  The fractions above use the published 8 TB/s peak.
+        n_copy = 1 << 30
+        src = torch.empty(n_copy, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(5):
+            dst.copy_(src)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbs = 2 * n_copy * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
 
-        def unfused():
-            h = torch.nn.functional.silu(fa) * fb
-            bs.bs_quant_1x128(h, step.qg, step.sg, step.qgT, step.sgT)
+        # Quantizers on cold caches: before each timed call, reading the 1 GiB
+        # scratch buffer evicts the inputs from L2 and the 256 MB last-level
+        # cache, so the rate is the HBM-bound one (median of 5).  The flush
+        # reads rather than writes: a written flush leaves the caches full of
+        # dirty lines, and writing those back would be charged to the
+        # quantizer.  Inside the step they may find part of their input cached.
+        flush_src = src.view(torch.int32)
+        flush_sink = torch.empty((), dtype=torch.int64, device="cuda")
+        for name, fn, work, unit in ks:
+            if unit != "GB/s":
+                continue
+            times = []
+            for r in range(5):
+                torch.sum(flush_src, dim=(0,), dtype=torch.int64, out=flush_sink)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            ms = sorted(times)[len(times) // 2]
+            rate = work / (ms * 1e-3) / 1e9
+            cold[name] = {"ms": round(ms, 4), "rate": round(rate, 1), "unit": "GB/s",
+                          "frac": round(rate / HBM_PEAK_GBS, 4), "work": work}
+        cold_gbs = sum(v["work"] for v in cold.values()) / (sum(v["ms"] for v in cold.values()) * 1e-3) / 1e9
+        for v in cold.values():
+            v.pop("work")
+        del src, dst, flush_src
+    del step, ks
+    torch.cuda.empty_cache()
 
-        f_ms, u_ms = median_ms(fused), median_ms(unfused)
-        f_bytes = M_ * N_ * (2 + 2 + 1 + 1) + 4 * (M_ * N_ // 128) * 2
-        fusion = {"shape": [M_, N_], "fused_ms": round(f_ms, 4), "unfused_ms": round(u_ms, 4),
-                  "fused_gbs": round(f_bytes / (f_ms * 1e-3) / 1e9, 1), "speedup": round(u_ms / f_ms, 2)}
+    # The dense workloads (one linear layer's forward, dgrad and wgrad): each
+    # timed the same way, with fewer steps; the gated FFN module at the same
+    # sizes (tokens M, dim K, hidden N) when asked for.
+    extra = {}
+    ffn = []
+    fusion = fusion_bwd = None
+    for x in extras:
+        wx = inputs.WORKLOADS[x]
+        sx = Step(wx, seed=args.seed, scale_pad=args.scale_pad)
+        pk, dx, dmx, msx = time_step(sx, min(args.steps, 20), min(args.warmup, 3), stream)
+        sm = summarize(wx, pk, msx)
+        extra[x] = {"ms_per_step": round(msx, 4), "value": round(sm["value"], 1), "unit": "TFLOP/s",
+                    "gemm_tflops": round(sm["gemm_tflops"], 1), "quant_gbs": round(sm["quant_gbs"], 1),
+                    "kernels": {k: {kk: vv for kk, vv in v.items() if kk != "work"} for k, v in pk.items()}}
+        if not args.no_fusion and fusion is None:
+            # Fusion next to the path: the FFN's gated activation h = silu(a) * b
+            # quantized for the next layer (rows + transposed columns), fused in
+            # one kernel versus torch's silu and mul followed by the quantizer.
+            # a, b are [M, N] bf16 (the step's output and grad_out buffers).
+            fa, fb = sx.out, sx.gout
+            M_, N_ = fa.shape
 
-        # ... and its backward: [da | db] from a, b, dh quantized (rows + columns
-        # of the [M, 2N] matrix) in one kernel, versus the same float32
-        # arithmetic in torch followed by the quantizer.
-        fd = inputs.bf16_normal((M_, N_), 0.01, args.seed + 30).cuda()
-        qd = torch.empty((M_, 2 * N_), dtype=torch.uint8, device="cuda")
-        sd = bs.empty_scales(2 * N_ // 128, M_, "cuda")
-        qdt = torch.empty((2 * N_, M_), dtype=torch.uint8, device="cuda")
-        sdt = bs.empty_scales(M_ // 128, 2 * N_, "cuda")
-        dab = torch.empty((M_, 2 * N_), dtype=torch.bfloat16, device="cuda")
+            def fused():
+                bs.bs_swiglu_quant_1x128(fa, fb, None, sx.qg, sx.sg, sx.qgT, sx.sgT)
 
-        def fused_bwd():
-            bs.bs_swiglu_bwd_quant_1x128(fa, fb, fd, None, qd, sd, qdt, sdt)
+            def unfused():
+                h = torch.nn.functional.silu(fa) * fb
+                bs.bs_quant_1x128(h, sx.qg, sx.sg, sx.qgT, sx.sgT)
 
-        def unfused_bwd():
-            a32, b32, d32 = fa.float(), fb.float(), fd.float()
-            sig = torch.sigmoid(a32)
-            dab[:, :N_] = d32 * b32 * sig * (1.0 + a32 * (1.0 - sig))
-            dab[:, N_:] = d32 * a32 * sig
-            bs.bs_quant_1x128(dab, qd, sd, qdt, sdt)
+            f_ms, u_ms = median_ms(fused), median_ms(unfused)
+            f_bytes = M_ * N_ * (2 + 2 + 1 + 1) + 4 * (M_ * N_ // 128) * 2
+            fusion = {"shape": [M_, N_], "fused_ms": round(f_ms, 4), "unfused_ms": round(u_ms, 4),
+                      "fused_gbs": round(f_bytes / (f_ms * 1e-3) / 1e9, 1), "speedup": round(u_ms / f_ms, 2)}
+            # ... and its backward: [da | db] from a, b, dh quantized (rows +
+            # columns of the [M, 2N] matrix) in one kernel, versus the same
+            # float32 arithmetic in torch followed by the quantizer.
+            fd = inputs.bf16_normal((M_, N_), 0.01, args.seed + 30).cuda()
+            qd = torch.empty((M_, 2 * N_), dtype=torch.uint8, device="cuda")
+            sd = bs.empty_scales(2 * N_ // 128, M_, "cuda")
+            qdt = torch.empty((2 * N_, M_), dtype=torch.uint8, device="cuda")
+            sdt = bs.empty_scales(M_ // 128, 2 * N_, "cuda")
+            dab = torch.empty((M_, 2 * N_), dtype=torch.bfloat16, device="cuda")
 
-        fb_ms, ub_ms = median_ms(fused_bwd), median_ms(unfused_bwd)
-        fb_bytes = M_ * N_ * (3 * 2 + 4 * 1) + 4 * (2 * M_ * N_ // 128) * 2
-        fusion_bwd = {"shape": [M_, N_], "fused_ms": round(fb_ms, 4), "unfused_ms": round(ub_ms, 4),
-                      "fused_gbs": round(fb_bytes / (fb_ms * 1e-3) / 1e9, 1), "speedup": round(ub_ms / fb_ms, 2)}
-        del qd, qdt, dab, fd
+            def fused_bwd():
+                bs.bs_swiglu_bwd_quant_1x128(fa, fb, fd, None, qd, sd, qdt, sdt)
 
-    # The gated FFN out_proj(silu(w1 x) * w2 x) as one module (shared input
-    # quantization, stacked w1/w2 GEMMs, the fused activation quantizer)
-    # against three Float8BlockwiseLinear layers with torch's silu and mul:
-    # one forward + backward each, dim = K and hidden = N of the workload.
-    ffn = None
-    if w.G == 1 and w.N % 512 == 0 and not args.no_ffn_module:
-        ffn = ffn_module_timing(w.M, w.K, w.N, median_ms, args.seed)
+            def unfused_bwd():
+                a32, b32, d32 = fa.float(), fb.float(), fd.float()
+                sig = torch.sigmoid(a32)
+                dab[:, :N_] = d32 * b32 * sig * (1.0 + a32 * (1.0 - sig))
+                dab[:, N_:] = d32 * a32 * sig
+                bs.bs_quant_1x128(dab, qd, sd, qdt, sdt)
+
+            fb_ms, ub_ms = median_ms(fused_bwd), median_ms(unfused_bwd)
+            fb_bytes = M_ * N_ * (3 * 2 + 4 * 1) + 4 * (2 * M_ * N_ // 128) * 2
+            fusion_bwd = {"shape": [M_, N_], "fused_ms": round(fb_ms, 4), "unfused_ms": round(ub_ms, 4),
+                          "fused_gbs": round(fb_bytes / (fb_ms * 1e-3) / 1e9, 1),
+                          "speedup": round(ub_ms / fb_ms, 2)}
+            del qd, qdt, dab, fd
+        del sx
         torch.cuda.empty_cache()
+        # The gated FFN out_proj(silu(w1 x) * w2 x) as one module (shared
+        # input quantization, stacked w1/w2 GEMMs, the fused activation
+        # quantizers) against three Float8BlockwiseLinear layers with torch's
+        # silu and mul: one forward + backward each.
+        if not args.no_ffn_module and wx.N % 512 == 0:
+            ffn.append(ffn_module_timing(wx.M, wx.K, wx.N, median_ms, args.seed))
+            torch.cuda.empty_cache()
 
     # MXFP8 grouped GEMMs (the pages' MoE recipe) at the pages' shapes,
     # forward and forward + backward with quantization, next to bf16
@@ -559,9 +712,16 @@ def main():
         cpu = {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
                "sample": desc, "seconds": round(secs, 2)}
 
+    cfg = {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "G": w.G,
+           "step": "quant A/W/W^T/grad_out + fwd, dgrad, wgrad GEMMs" +
+                   (" (grouped: GROUP_M fwd/dgrad, GROUP_K wgrad)" if w.G > 1 else "")}
+    if cfg_groups is not None:
+        cfg["group_sizes"] = cfg_groups
+    if args.scale_pad:
+        cfg["scale_pad"] = args.scale_pad
     line = {
         "metric": "FP8 blockwise GEMM TFLOP/s fwd+bwd, % of FP8 MFMA peak; quantizer GB/s",
-        "value": round(value, 1),
+        "value": round(summ["value"], 1),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -572,22 +732,24 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8_e4m3 (fp32 accumulate)",
         "data": "synthetic (seeded N(0, s) bf16, resident in HBM)",
-        "config": {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "G": w.G,
-                   "step": "quant A/W/W^T/grad_out + fwd, dgrad, wgrad GEMMs"},
-        "gemm_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1),
-        "gemm_frac_of_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
-        "quant_gbs": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
-        "quant_frac_of_hbm": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "hbm_copy_gbs": round(copy_gbs, 1),
-        "quant_cold_gbs": round(cold_gbs, 1),
-        "quant_cold_frac_of_hbm": round(cold_gbs / HBM_PEAK_GBS, 4),
+        "config": cfg,
+        "gemm_tflops": round(summ["gemm_tflops"], 1),
+        "gemm_frac_of_peak": round(summ["gemm_tflops"] / FP8_PEAK_TFLOPS, 4),
+        "quant_gbs": round(summ["quant_gbs"], 1),
+        "quant_frac_of_hbm": round(summ["quant_gbs"] / HBM_PEAK_GBS, 4),
+        "clocks": clocks.summary(),
+        "inputs_sha256": digest,
+        "hbm_copy_gbs": None if copy_gbs is None else round(copy_gbs, 1),
+        "quant_frac_of_copy": None if copy_gbs is None else round(summ["quant_gbs"] / copy_gbs, 4),
+        "quant_cold_gbs": None if cold_gbs is None else round(cold_gbs, 1),
+        "quant_cold_frac_of_hbm": None if cold_gbs is None else round(cold_gbs / HBM_PEAK_GBS, 4),
         "quant_cold": cold,
+        "kernels": per_kernel,
+        "extra_configs": extra,
         "swiglu_quant_fusion": fusion,
         "swiglu_bwd_quant_fusion": fusion_bwd,
         "gated_ffn_module": ffn,
         "mxfp8_grouped_mm": mxfp8,
-        "quant_frac_of_copy": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / copy_gbs, 4),
-        "kernels": per_kernel,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

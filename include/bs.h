@@ -130,6 +130,11 @@ bs_status bs_quant_1x128(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x,
  *   q_row/s_row, q_col/s_col  as in bs_quant_1x128 (blocks of h).
  * The kernel evaluates in fp32 and switches to float64 for the rare values
  * whose fp32 result lies within its error bound of a bf16 rounding tie.
+ * Finite a, b can give |silu(a) * b| above the bf16 maximum: h is then +-inf
+ * (the rounding overflows, and h is written so when requested), which is
+ * outside the quantizer's finite domain -- the codes and the scale of every
+ * 1x128 block (row and column) holding such an h are unspecified; all other
+ * blocks are exact.
  * Pages: "add FSDP and TP tests for Float8BlockwiseLinear", summary (the
  * ToyModel FFN: w1 and w2 feed out_proj); the prototype page, description
  * (quantization as separate kernels is the overhead to remove).
@@ -158,6 +163,8 @@ bs_status bs_swiglu_quant_1x128(const uint16_t* a, const uint16_t* b, int64_t R,
  *   q_col, s_col   both NULL or both set: [2C, R] codes, ld_qc >= R;
  *                  s_col[(r / 128) * ld_sc + c], ld_sc >= 2C
  *   C % 128 == 0; R % 128 == 0 when the col output is requested.
+ * As in the forward, a da or db that overflows bf16 is +-inf, and the codes
+ * and scale of every block holding one are unspecified.
  * Errors as bs_quant_1x128.
  * Pages: "add FSDP and TP tests for Float8BlockwiseLinear", summary (the
  * ToyModel FFN and its backward); the prototype page, description.

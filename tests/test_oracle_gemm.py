@@ -63,6 +63,33 @@ def test_general_scales_vs_rationals(rng):
             assert abs(Fraction(d[m, n]) - tot) <= mag * Fraction(1, 10 ** 12)
 
 
+def test_128x128_b_scales_vs_rationals_several_row_and_k_blocks(rng):
+    """128x128 B scales with N = 384 (three row blocks) and K = 384 (three K
+    blocks), a distinct scale per (row block, K block): every sampled output
+    against a Fraction sum whose B scale is looked up element by element as
+    sb[n // 128][k // 128] (no expansion of the scale array).  A scale taken
+    from the wrong row block or K block, or a transposed scale array, moves
+    the result far outside the 1e-12 bound."""
+    M, N, K = 6, 384, 384
+    qa, qb = rand_codes(rng, (M, K)), rand_codes(rng, (N, K))
+    sa = (rng.random((M, 3)) * 1e-2 + 1e-4).astype(np.float32)
+    # distinct, well separated scales: 2^(3i + j) times a random mantissa
+    sb = np.array([[(1.0 + rng.random()) * 2.0 ** (3 * i + j - 4) for j in range(3)] for i in range(3)],
+                  dtype=np.float32)
+    assert len(set(sb.ravel().tolist())) == 9
+    d = gemm.scaled_mm(qa, sa, qb, sb, 128)
+    for m in range(M):
+        for n in list(range(0, N, 37)) + [127, 128, 255, 256, 383]:
+            tot = Fraction(0)
+            mag = Fraction(0)
+            for k in range(K):
+                t = (Fraction(float(e4m3.DECODE[qa[m, k]])) * Fraction(float(sa[m, k // 128]))
+                     * Fraction(float(e4m3.DECODE[qb[n, k]])) * Fraction(float(sb[n // 128, k // 128])))
+                tot += t
+                mag += abs(t)
+            assert abs(Fraction(d[m, n]) - tot) <= mag * Fraction(1, 10 ** 12), (m, n)
+
+
 def test_identity_b_returns_dequantized_a(rng):
     M, K = 64, 256
     qa = rand_codes(rng, (M, K))

@@ -72,8 +72,9 @@ class OracleLinear(torch.nn.Module):
 
 
 class _OracleSwiGLUFn(torch.autograd.Function):
-    """h = silu(a) * b rounded once to bf16 by the oracle; backward in float64
-    (da = dh b silu'(a), db = dh silu(a)), rounded to bf16."""
+    """h = silu(a) * b rounded once to bf16 by the oracle; the backward is the
+    oracle's (da = dh b silu'(a), db = dh silu(a), each rounded once to bf16
+    from float64)."""
 
     @staticmethod
     def forward(ctx, a, b):
@@ -84,12 +85,11 @@ class _OracleSwiGLUFn(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, dh):
+        from oracle import swiglu as oswiglu
         a, b = ctx.saved_tensors
-        a64, b64, dh64 = a.double(), b.double(), dh.double()
-        sig = torch.sigmoid(a64)
-        da = dh64 * b64 * sig * (1.0 + a64 * (1.0 - sig))
-        db = dh64 * a64 * sig
-        return da.to(torch.bfloat16), db.to(torch.bfloat16)
+        da, db = oswiglu.swiglu_backward(_bits(a), _bits(b), _bits(dh.to(torch.bfloat16)))
+        as_bf16 = lambda v: torch.from_numpy(v.view(np.int16).copy()).view(torch.bfloat16).view(a.shape)  # noqa: E731
+        return as_bf16(da), as_bf16(db)
 
 
 class OracleGatedFFN(torch.nn.Module):
