@@ -61,6 +61,7 @@ KERNEL_SYMBOL = {
     "gemm_fwd": "gemm_kernel<0, false, false>",
     "gemm_dgrad": "gemm_kernel<0, false, false>",
     "gemm_wgrad": "gemm_kernel<0, true, false>",
+    "gemm_wgrad_split": "gemm_sk_kernel<true, false>",
     "grouped_gemm_fwd": "gemm_kernel<1, false, false>",
     "grouped_gemm_dgrad": "gemm_kernel<1, false, false>",
     "grouped_gemm_wgrad": "gemm_kernel<2, true, false>",
@@ -71,6 +72,7 @@ KERNEL_SYMBOL = {
 # while these are unchanged)
 KERNEL_SOURCES = {
     "gemm_kernel": ["bs_gemm.hip", "bs_kernels.h"],
+    "gemm_sk_kernel": ["bs_gemm.hip", "bs_kernels.h"],
     "mx_gemm_kernel": ["bs_gemm.hip", "bs_kernels.h"],
     "quant_": ["bs_quant.hip", "bs_device.h", "bs_kernels.h", "bs_mx.h"],
     "swiglu_bwd_quant_kernel": ["bs_quant.hip", "bs_device.h", "bs_kernels.h", "bs_mx.h"],
@@ -91,15 +93,16 @@ def kernel_source_hash(symbol):
     return h.hexdigest()[:16]
 
 
-def counter_traffic(workload, kernel):
+def counter_traffic(workload, kernel, split=False):
     """HBM-side bytes per launch of `kernel` from the committed rocprofv3
     counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by its reading of a
     known-size copy), or None when there is none or the kernel sources have
-    changed since it was taken."""
+    changed since it was taken.  ``split``: the wgrad ran as its stream-K
+    kernel."""
     path = os.path.join(ROOT, "profiles", f"{workload}_rocprof.txt")
     if not os.path.exists(path):
         return None
-    sym = KERNEL_SYMBOL.get(kernel)
+    sym = KERNEL_SYMBOL.get(kernel + "_split" if split else kernel)
     cur = kernel_source_hash(sym) if sym else None
     for line in open(path):
         if line.startswith("traffic_bytes ") and sym and sym in line:
@@ -174,8 +177,10 @@ class Step:
                                                      out=self.out), gemm_flops, "TFLOP/s"),
                 ("gemm_dgrad", lambda: bs.bs_scaled_mm(self.qg, self.sg, self.qwT[0], self.swT[0],
                                                        bs.BS_SCALE_128X128, out=self.gin), gemm_flops, "TFLOP/s"),
-                ("gemm_wgrad", lambda: bs.bs_scaled_mm(self.qgT, self.sgT, self.qaT, self.saT, bs.BS_SCALE_1X128,
-                                                       out=self.gw), gemm_flops, "TFLOP/s"),
+                # stream-K form: splits a ragged last round of tiles along K
+                # (and is the plain kernel when the tiles fill every round)
+                ("gemm_wgrad", lambda: bs.bs_scaled_mm_ws(self.qgT, self.sgT, self.qaT, self.saT,
+                                                          bs.BS_SCALE_1X128, out=self.gw), gemm_flops, "TFLOP/s"),
             ]
         else:
             ks += [
@@ -331,6 +336,11 @@ def mx_grouped_timing(median_ms, seed, which=None):
         del x, wt, dy
         torch.cuda.empty_cache()
     return rows
+
+
+def wgrad_split(w):
+    """Whether the dense wgrad of workload w runs as the stream-K kernel."""
+    return w.G == 1 and bs.bs_scaled_mm_workspace_bytes(w.N, w.K, w.M, bs.BS_SCALE_1X128) > 0
 
 
 def input_digest(step):
@@ -557,7 +567,7 @@ def main():
         "peak": dom_peak,
         "unit": d["unit"],
         "frac": round(dom_rate / dom_peak, 4),
-        "traffic": counter_traffic(w.name, dom),
+        "traffic": counter_traffic(w.name, dom, split=dom == "gemm_wgrad" and wgrad_split(w)),
         "avg_ms": round(dom_ms, 4),
         "work_per_launch": d["work"],
     }

@@ -26,8 +26,11 @@ from .binding import (  # noqa: F401
     bs_swiglu_bwd_quant_1x128,
     bs_swiglu_quant_1x128,
     bs_scaled_mm,
+    bs_scaled_mm_workspace_bytes,
+    bs_scaled_mm_ws,
     empty_mx_scales,
     empty_scales,
+    streamk_workspace,
 )
 from .linear import Float8BlockwiseLinear, float8_blockwise_linear, swap_linear_layers  # noqa: F401,E402
 from .ffn import Float8BlockwiseGatedFFN, float8_blockwise_gated_ffn  # noqa: F401,E402

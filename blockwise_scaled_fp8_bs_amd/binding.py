@@ -385,6 +385,61 @@ def bs_scaled_mm(a, sa, b, sb, b_kind, out=None, out_dtype=torch.bfloat16, strea
     return out
 
 
+def bs_scaled_mm_workspace_bytes(M, N, K, b_kind, out_dtype=torch.bfloat16):
+    """Workspace bytes bs_scaled_mm_ws uses for this problem on the current device (0: no split)."""
+    dt = {torch.bfloat16: BS_OUT_BF16, torch.float32: BS_OUT_F32}.get(out_dtype)
+    _require(dt is not None, "out_dtype must be bfloat16 or float32")
+    return int(_lib.load().bs_scaled_mm_workspace_bytes(M, N, K, b_kind, dt))
+
+
+_WORKSPACES = {}
+
+
+def streamk_workspace(nbytes, device=None):
+    """A zero-initialised device workspace of at least ``nbytes`` for
+    bs_scaled_mm_ws, cached per device and grown on demand (torch owns the
+    memory).  Calls that share it must not overlap in time: use it from one
+    stream."""
+    device = torch.device("cuda" if device is None else device)
+    if device.index is None:
+        device = torch.device(device.type, torch.cuda.current_device())
+    ws = _WORKSPACES.get(device)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
+        _WORKSPACES[device] = ws
+    return ws
+
+
+def bs_scaled_mm_ws(a, sa, b, sb, b_kind, workspace=None, out=None, out_dtype=torch.bfloat16, stream=None):
+    """bs_scaled_mm with a device workspace (uint8 GPU tensor, 256-byte
+    aligned, first 4096 bytes zero before first use) that lets the kernel
+    split a ragged last round of tiles along K; see include/bs.h.  With
+    ``workspace=None`` the per-device cached workspace (streamk_workspace)
+    sized for this problem is used."""
+    _mat(a, "a", torch.uint8)
+    _mat(b, "b", torch.uint8)
+    M, K = a.shape
+    N, Kb = b.shape
+    _require(K == Kb, f"a is [M, {K}] but b is [N, {Kb}]: both must be contiguous along the same K")
+    ld_sa = _scale(sa, "sa", K // 128, M)
+    ld_sb = _scale(sb, "sb", K // 128, N if b_kind == BS_SCALE_1X128 else (N + 127) // 128)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    if workspace is None:
+        workspace = streamk_workspace(bs_scaled_mm_workspace_bytes(M, N, K, b_kind, out.dtype), a.device)
+    _require(workspace.dtype == torch.uint8 and workspace.is_cuda and workspace.is_contiguous(),
+             "workspace must be a contiguous uint8 GPU tensor")
+    _mat(out, "out", out.dtype)
+    _require(tuple(out.shape) == (M, N), f"out must be [{M}, {N}]")
+    dt = {torch.bfloat16: BS_OUT_BF16, torch.float32: BS_OUT_F32}.get(out.dtype)
+    _require(dt is not None, "out must be bfloat16 or float32")
+    _check(_lib.load().bs_scaled_mm_ws(M, N, K, _ptr(a), _ld(a), _ptr(sa), ld_sa, BS_SCALE_1X128, _ptr(b), _ld(b),
+                                       _ptr(sb), ld_sb, b_kind, _ptr(out), _ld(out), dt, _ptr(workspace),
+                                       workspace.numel(), _stream(stream)),
+           "bs_scaled_mm_ws")
+    return out
+
+
 def bs_grouped_scaled_mm(mode, group_end, a, sa, b, sb, b_kind, out=None, out_dtype=torch.bfloat16,
                          stream=None):
     """Grouped (MoE) scaled GEMM.

@@ -508,6 +508,60 @@ bs_status bs_scaled_mm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_
                                       d_dtype == BS_OUT_F32, stream), fn);
 }
 
+namespace {
+
+// The dense problem of bs_scaled_mm as kernel arguments (validated).
+bs::GemmArgs dense_args(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const float* sa,
+                        int64_t ld_sa, const uint8_t* b, int64_t ldb, const float* sb, int64_t ld_sb, void* d,
+                        int64_t ldd) {
+    bs::GemmArgs g{};
+    g.M = M; g.N = N; g.K = K;
+    g.a = a; g.lda = lda; g.sa = sa; g.ld_sa = ld_sa;
+    g.b = b; g.ldb = ldb; g.sb = sb; g.ld_sb = ld_sb;
+    g.d = d; g.ldd = ldd;
+    g.G = 1;
+    g.tiles_m = (M + 255) / 256;
+    g.tiles_n = (N + 255) / 256;
+    g.num_tiles = g.tiles_m * g.tiles_n;
+    return g;
+}
+
+}  // namespace
+
+int64_t bs_scaled_mm_workspace_bytes(int64_t M, int64_t N, int64_t K, bs_scale_kind b_kind, bs_dtype d_dtype) {
+    if (M <= 0 || N <= 0 || K <= 0 || N % 128 || K % 128) return 0;
+    if (b_kind != BS_SCALE_1X128 && b_kind != BS_SCALE_128X128) return 0;
+    const bs::GemmArgs g = dense_args(M, N, K, nullptr, K, nullptr, M, nullptr, K, nullptr, N, nullptr, N);
+    return bs::streamk_workspace_bytes(bs::plan_streamk(
+        g, b_kind == BS_SCALE_1X128 ? bs::kScale1x128 : bs::kScale128x128, d_dtype == BS_OUT_F32));
+}
+
+bs_status bs_scaled_mm_ws(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const float* sa,
+                          int64_t ld_sa, bs_scale_kind a_kind, const uint8_t* b, int64_t ldb, const float* sb,
+                          int64_t ld_sb, bs_scale_kind b_kind, void* d, int64_t ldd, bs_dtype d_dtype,
+                          void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+    static const char* fn = "bs_scaled_mm_ws";
+    REQUIRE(a_kind == BS_SCALE_1X128, BS_ERR_MODE, "a_kind=%d: A takes 1x128 scales (BS_SCALE_1X128 = 4)",
+            (int)a_kind);
+    bs_status st = check_gemm_common(fn, M, N, K, a, lda, sa, ld_sa, b, ldb, sb, ld_sb, b_kind, d, ldd, d_dtype);
+    if (st != BS_OK) return st;
+    REQUIRE(ld_sa >= M, BS_ERR_LAYOUT, "ld_sa=%lld < M=%lld: sa is K-major [K/128][ld_sa >= M]",
+            (long long)ld_sa, (long long)M);
+    const int64_t nrows_sb = b_kind == BS_SCALE_1X128 ? N : N / 128;
+    REQUIRE(ld_sb >= nrows_sb, BS_ERR_LAYOUT, "ld_sb=%lld < %lld: sb is K-major [K/128][ld_sb >= %s]",
+            (long long)ld_sb, (long long)nrows_sb, b_kind == BS_SCALE_1X128 ? "N" : "N/128");
+    REQUIRE(workspace_bytes >= 0, BS_ERR_LAYOUT, "workspace_bytes=%lld must be >= 0", (long long)workspace_bytes);
+    REQUIRE(workspace || workspace_bytes == 0, BS_ERR_NULL, "workspace is NULL but workspace_bytes=%lld",
+            (long long)workspace_bytes);
+    REQUIRE(workspace == nullptr || ((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0), BS_ERR_ALIGN,
+            "workspace must be 256-byte aligned");
+    if (M == 0 || N == 0) return ok();
+    const bs::GemmArgs g = dense_args(M, N, K, a, lda, sa, ld_sa, b, ldb, sb, ld_sb, d, ldd);
+    return hip_status(bs::launch_gemm_streamk(g, b_kind == BS_SCALE_1X128 ? bs::kScale1x128 : bs::kScale128x128,
+                                              d_dtype == BS_OUT_F32, workspace, workspace_bytes, stream),
+                      fn);
+}
+
 bs_status bs_grouped_scaled_mm(bs_group_mode mode, int64_t G, int64_t M, int64_t N, int64_t K,
                                const int32_t* group_end, const uint8_t* a, int64_t lda, const float* sa,
                                int64_t ld_sa, const uint8_t* b, int64_t stride_bg, int64_t ldb, const float* sb,

@@ -116,7 +116,70 @@ struct Tile {
     int32_t n0;
     int32_t kb0, kb1;    // K blocks [kb0, kb1)
     int32_t g;           // group: whose B (GROUP_M) or which D (GROUP_K)
+    int32_t role;        // stream-K: 0 whole tile, 1 later K blocks (partial for the owner), 2 owner
+    int32_t sk_last;     // owner: the last workgroup holding a part of this tile
 };
+
+// Stream-K work item q of this workgroup (dense problems): first the whole
+// tiles q * grid + blockIdx.x of the leading rounds, then the pieces of the
+// split tiles that fall into this workgroup's share [i0, i1) of their K
+// iterations, in order.  Shares are dealt by a virtual index v that gives the
+// workgroups of one XCD consecutive shares (so an XCD works on a few
+// neighbouring tiles and shares their operand panels in its L2).  A piece
+// that starts a tile's K range is its owner: it adds the partial tiles of
+// the later pieces (virtual workgroups v + 1 .. sk_last, each of which has
+// that piece as its first) before storing D.
+__device__ __forceinline__ int64_t sk_virtual(const GemmArgs& p) {
+    return (int64_t)blockIdx.x < p.sk_wgs ? xcd_remap(blockIdx.x, p.sk_wgs) : (int64_t)blockIdx.x;
+}
+
+__device__ __forceinline__ bool sk_has_work(const GemmArgs& p, int64_t q) {
+    const int64_t P = gridDim.x, w = sk_virtual(p);
+    const int64_t dp_rounds = p.sk_dp_tiles / P;
+    if (q < dp_rounds) return true;
+    if (w >= p.sk_wgs) return false;
+    const int64_t nkb = p.K / BK, I = p.sk_tiles * nkb;
+    const int64_t i0 = w * I / p.sk_wgs, i1 = (w + 1) * I / p.sk_wgs;
+    return (i0 / nkb + (q - dp_rounds)) * nkb < i1;
+}
+
+__device__ __forceinline__ bool sk_work(const GemmArgs& p, int64_t q, Tile& t) {
+    const int64_t P = gridDim.x, w = sk_virtual(p);
+    const int64_t nkb = p.K / BK;
+    const int64_t dp_rounds = p.sk_dp_tiles / P;
+    int64_t L;
+    t.g = 0;
+    t.role = 0;
+    t.sk_last = 0;
+    t.m_end = (int32_t)p.M;
+    if (q < dp_rounds) {
+        L = xcd_remap(q * P + blockIdx.x, p.sk_dp_tiles);
+        t.kb0 = 0;
+        t.kb1 = (int32_t)nkb;
+    } else {
+        if (w >= p.sk_wgs) return false;
+        const int64_t I = p.sk_tiles * nkb;
+        const int64_t i0 = w * I / p.sk_wgs, i1 = (w + 1) * I / p.sk_wgs;
+        const int64_t tt = i0 / nkb + (q - dp_rounds);
+        const int64_t s = i0 > tt * nkb ? i0 : tt * nkb;
+        const int64_t e = i1 < (tt + 1) * nkb ? i1 : (tt + 1) * nkb;
+        if (s >= e) return false;
+        L = p.sk_dp_tiles + tt;
+        t.kb0 = (int32_t)(s - tt * nkb);
+        t.kb1 = (int32_t)(e - tt * nkb);
+        if (t.kb0 > 0) {
+            t.role = 1;
+        } else if (t.kb1 < nkb) {
+            t.role = 2;
+            t.sk_last = (int32_t)(((tt + 1) * nkb * p.sk_wgs - 1) / I);
+        }
+    }
+    int64_t tm, tn;
+    grouped_order(L, p.tiles_m, p.tiles_n, tm, tn);
+    t.m0 = (int32_t)(tm * BM);
+    t.n0 = (int32_t)(tn * BN);
+    return true;
+}
 
 // Number of tiles; for GROUP_M also the tile rows summed over the groups
 // (group ends clamped to be monotone in [0, M]).
@@ -139,6 +202,8 @@ template <int KIND>
 __device__ __forceinline__ void resolve_tile(const GemmArgs& p, int64_t idx, int64_t total, int64_t rows,
                                              const int32_t* group_by_rank, const SliceTables& st, Tile& t) {
     t.g = 0;
+    t.role = 0;
+    t.sk_last = 0;
     t.kb0 = 0;
     t.kb1 = (int32_t)(p.K / BK);
     const int64_t L = KIND == kGroupK ? 0 : xcd_remap(idx, total);
@@ -302,11 +367,12 @@ __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" :
 // lane offsets.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-template <int KIND, int SC, bool OUT_F32>
+template <int KIND, int SC, bool OUT_F32, bool SK = false>
 __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
     __shared__ Smem sm;  // one per instantiation; each kernel below uses one
     constexpr bool B1X128 = SC == kScale1x128;
     constexpr bool MX = SC == kScaleMx;
+    static_assert(!SK || KIND == kDense, "stream-K splits dense problems only");
     const int t = threadIdx.x;
     const int lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = w / WAVES_N, wn = w % WAVES_N;
@@ -314,8 +380,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
 
     int64_t rows_total;
     const int64_t total = tile_total<KIND>(p, rows_total);
-    int64_t idx = blockIdx.x;
-    if (idx >= total) return;
+    int64_t idx = blockIdx.x;  // tile index (stream-K: work item counter q)
+    if (SK) {
+        Tile t0;
+        idx = 0;
+        if (!sk_work(p, 0, t0)) return;
+    } else if (idx >= total) {
+        return;
+    }
 
     if (KIND == kGroupM && p.G <= kMaxSlicedGroups) {
         // Tile-row order for GROUP_M: slice x (of 8) of every group in turn,
@@ -503,7 +575,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
     };
 
     Tile cur;
-    resolve_tile<KIND>(p, idx, total, rows_total, sm.group_by_rank, slices, cur);
+    if (SK)
+        sk_work(p, idx, cur);
+    else
+        resolve_tile<KIND>(p, idx, total, rows_total, sm.group_by_rank, slices, cur);
     Operands ops = make_operands<KIND, SC>(p, cur);
     int32_t nkb = cur.kb1 - cur.kb0;
     int s = 0;  // LDS stage holding the current K block
@@ -515,13 +590,16 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
     for (;;) {
         // The next tile of this workgroup: its first K block is loaded
         // during the last K block of this one.
-        const int64_t nidx = idx + gridDim.x;
-        const bool has_next = nidx < total;
+        const int64_t nidx = SK ? idx + 1 : idx + gridDim.x;
+        const bool has_next = SK ? sk_has_work(p, nidx) : nidx < total;
         Tile nxt = cur;
         Operands nops = ops;
         bool next_resolved = false;
         auto load_next = [&](int stage) {
-            resolve_tile<KIND>(p, nidx, total, rows_total, sm.group_by_rank, slices, nxt);
+            if (SK)
+                sk_work(p, nidx, nxt);
+            else
+                resolve_tile<KIND>(p, nidx, total, rows_total, sm.group_by_rank, slices, nxt);
             nops = make_operands<KIND, SC>(p, nxt);
             if (nxt.kb1 > nxt.kb0) issue_loads(nops, nxt.kb0, stage);
             next_resolved = true;
@@ -625,10 +703,79 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
             s ^= 1;
         }
 
+        // ---- stream-K: a piece after a tile's first K blocks leaves its
+        // partial tile (lane-major, as the registers hold it) in this
+        // workgroup's slot and raises its flag; the owner adds the partials of
+        // virtual workgroups v + 1 .. sk_last, in that order, and clears their
+        // flags ----
+        bool store_d = true;
+        // The slot is addressed through a buffer descriptor: lane offset in one
+        // VGPR, the MFMA tile's 1 KiB step as the uniform offset.  Partial
+        // tiles are written and read at device scope (cache policy SC1: the
+        // stores go through this XCD's L2 to memory, the loads fetch from
+        // there), so that no cache-wide write-back or invalidate is needed
+        // -- other workgroups on the same XCD keep their cached operands.
+        const int sk_voff = (w * TM * TN * 64 + lane) * 16;
+        constexpr int kDeviceScope = 16;  // SC1
+        const int sk_v = SK ? (int)sk_virtual(p) : 0;
+        if (SK && cur.role == 1) {
+            const __amdgpu_buffer_rsrc_t slot = __builtin_amdgcn_make_buffer_rsrc(
+                p.sk_partial + (int64_t)sk_v * (BM * BN), (short)0, BM * BN * 4, 0x00020000);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), slot, sk_voff,
+                                                           (i * TN + j) * 1024, kDeviceScope);
+            // every store of the partial has reached device scope before the
+            // flag is raised
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (t == 0) __hip_atomic_store(&p.sk_flag[sk_v], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            store_d = false;
+        } else if (SK && cur.role == 2) {
+            bool lost = false;
+            for (int c = sk_v + 1; c <= cur.sk_last; ++c) {
+                // the flag is raised by a workgroup that has already finished
+                // its piece (pieces are its first work after the whole tiles);
+                // the bound only guards against a workspace whose flags were
+                // not zero on entry
+                int n = 0;
+                while (__hip_atomic_load(&p.sk_flag[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u &&
+                       n < (1 << 22)) {
+                    __builtin_amdgcn_s_sleep(2);
+                    ++n;
+                }
+                lost = lost || n >= (1 << 22);
+                // the loads below are issued after the flag was seen set
+                asm volatile("" ::: "memory");
+                const __amdgpu_buffer_rsrc_t slot = __builtin_amdgcn_make_buffer_rsrc(
+                    p.sk_partial + (int64_t)c * (BM * BN), (short)0, BM * BN * 4, 0x00020000);
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] += __builtin_bit_cast(
+                            v4f, __builtin_amdgcn_raw_buffer_load_b128(slot, sk_voff, (i * TN + j) * 1024,
+                                                                       kDeviceScope));
+            }
+            if (lost) {  // never expected: make the tile visibly wrong rather than silently short
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{NAN, NAN, NAN, NAN};
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();  // every wave has read the partials
+            if (t == 0)
+                for (int c = sk_v + 1; c <= cur.sk_last; ++c)
+                    __hip_atomic_store(&p.sk_flag[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+
         // ---- epilogue: stage each 16 x 64 block of the wave's tile in the
         // free LDS stage (s ^ 1: read for the last time before the barrier
         // above), then store whole 16-byte chunks of rows ----
-        {
+        if (store_d) {
             constexpr int ESZ = OUT_F32 ? 4 : 2;
             constexpr int PITCH = WN * ESZ + 16;     // padded row: 16 lanes of a write hit distinct banks
             constexpr int CPR = WN * ESZ / 16;       // 16-byte chunks per row
@@ -693,6 +840,11 @@ __global__ __launch_bounds__(NT) void mx_gemm_kernel(GemmArgs p) {
     gemm_body<KIND, kScaleMx, OUT_F32>(p);
 }
 
+template <bool B1X128, bool OUT_F32>
+__global__ __launch_bounds__(NT) void gemm_sk_kernel(GemmArgs p) {
+    gemm_body<kDense, B1X128 ? kScale1x128 : kScale128x128, OUT_F32, true>(p);
+}
+
 // Persistent grid: as many workgroups as fit on the device at once, never
 // more than the tiles.
 template <typename Kern>
@@ -731,7 +883,78 @@ hipError_t launch_kind(const GemmArgs& a, ScaleMode scales, bool out_f32, hipStr
     }
 }
 
+template <typename Kern>
+hipError_t launch_grid(Kern kernel, unsigned grid, const GemmArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+// Smallest K share of a stream-K workgroup, in K blocks.
+constexpr int64_t kSkMinBlocks = 4;
+
+template <typename Kern>
+StreamK plan_for(Kern kernel, const GemmArgs& a) {
+    StreamK sk{0, 0, 0, 0};
+    const int64_t tiles = a.tiles_m * a.tiles_n;
+    const int64_t P = persistent_grid(kernel, (int64_t)1 << 40);  // every resident workgroup
+    const int64_t nkb = a.K / BK;
+    sk.grid = tiles < P ? tiles : P;
+    if (tiles <= 0 || P <= 1 || nkb < 2 * kSkMinBlocks) return sk;
+    const int64_t rest = tiles % P;
+    // A last round at least 3/4 full is left as it is: the split costs each
+    // of its workgroups a second prologue and epilogue and a partial tile
+    // through memory, and with a quarter of the CUs idle the busy ones run
+    // at a higher clock (measured: 224 tiles on 256 CUs ran 11 % slower
+    // split; 128 tiles over a full round ran 5 % faster).
+    if (rest == 0 || 4 * rest > 3 * P) return sk;
+    const int64_t iters = rest * nkb;
+    int64_t wgs = iters / kSkMinBlocks;
+    wgs = wgs < P ? wgs : P;
+    if (wgs <= rest) return sk;  // no more workgroups than split tiles: no gain
+    sk.grid = P;
+    sk.dp_tiles = tiles - rest;
+    sk.sk_tiles = rest;
+    sk.sk_wgs = wgs;
+    return sk;
+}
+
+template <bool B1X128>
+StreamK plan_kind(const GemmArgs& a, bool out_f32) {
+    return out_f32 ? plan_for(gemm_sk_kernel<B1X128, true>, a) : plan_for(gemm_sk_kernel<B1X128, false>, a);
+}
+
+constexpr int64_t kSkFlagBytes = 4096;  // flag words, one per workgroup (room for 1024)
+
 }  // namespace
+
+StreamK plan_streamk(const GemmArgs& a, ScaleMode scales, bool out_f32) {
+    return scales == kScale1x128 ? plan_kind<true>(a, out_f32) : plan_kind<false>(a, out_f32);
+}
+
+int64_t streamk_workspace_bytes(const StreamK& sk) {
+    if (sk.sk_tiles == 0) return 0;
+    return kSkFlagBytes + sk.sk_wgs * (int64_t)(BM * BN) * 4;
+}
+
+hipError_t launch_gemm_streamk(const GemmArgs& a, ScaleMode scales, bool out_f32, void* workspace,
+                               int64_t workspace_bytes, hipStream_t stream) {
+    const StreamK sk = plan_streamk(a, scales, out_f32);
+    const int64_t need = streamk_workspace_bytes(sk);
+    if (sk.sk_tiles == 0 || sk.sk_wgs * 4 > kSkFlagBytes || workspace == nullptr || workspace_bytes < need)
+        return launch_gemm(a, kDense, scales, out_f32, stream);
+    GemmArgs g = a;
+    g.sk_dp_tiles = sk.dp_tiles;
+    g.sk_tiles = sk.sk_tiles;
+    g.sk_wgs = sk.sk_wgs;
+    g.sk_flag = static_cast<uint32_t*>(workspace);
+    g.sk_partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + kSkFlagBytes);
+    const unsigned grid = (unsigned)sk.grid;
+    if (scales == kScale1x128)
+        return out_f32 ? launch_grid(gemm_sk_kernel<true, true>, grid, g, stream)
+                       : launch_grid(gemm_sk_kernel<true, false>, grid, g, stream);
+    return out_f32 ? launch_grid(gemm_sk_kernel<false, true>, grid, g, stream)
+                   : launch_grid(gemm_sk_kernel<false, false>, grid, g, stream);
+}
 
 hipError_t launch_gemm(const GemmArgs& a, GroupKind kind, ScaleMode scales, bool out_f32, hipStream_t stream) {
     switch (kind) {

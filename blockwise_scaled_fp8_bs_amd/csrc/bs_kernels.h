@@ -89,6 +89,22 @@ struct GemmArgs {
     // launch geometry
     int64_t tiles_m, tiles_n;  // tiles of the dense problem (GROUP_K: per group)
     int64_t num_tiles;         // grid size (an upper bound for GROUP_M)
+    // stream-K split of a dense problem (set by launch_gemm_streamk): the
+    // first sk_dp_tiles tiles are whole work items dealt round-robin over the
+    // grid; the K iterations of the remaining sk_tiles tiles are divided
+    // evenly over sk_wgs workgroups; sk_flag[p] / sk_partial + p * 256 * 256
+    // hold workgroup p's partial tile for its owner (workspace)
+    int64_t sk_dp_tiles, sk_tiles, sk_wgs;
+    uint32_t* sk_flag;
+    float* sk_partial;
+};
+
+// Stream-K decomposition of a dense GEMM for a given grid.
+struct StreamK {
+    int64_t grid;      // persistent workgroups
+    int64_t dp_tiles;  // whole tiles (a multiple of grid)
+    int64_t sk_tiles;  // tiles split over workgroups (0: no split)
+    int64_t sk_wgs;    // workgroups sharing the split tiles' K iterations
 };
 
 hipError_t launch_quant_1x128(const Quant1x128Args& a, bool row, bool col, bool swiglu, hipStream_t stream);
@@ -96,6 +112,15 @@ hipError_t launch_quant_128x128(const Quant128Args& a, Quant128Mode mode, hipStr
 hipError_t launch_swiglu_bwd_quant(const SwigluBwdArgs& a, bool row, bool col, hipStream_t stream);
 
 hipError_t launch_gemm(const GemmArgs& a, GroupKind kind, ScaleMode scales, bool out_f32, hipStream_t stream);
+
+// Dense GEMM with the ragged last round of tiles split along K (stream-K)
+// when the workspace holds the partial tiles; otherwise as launch_gemm.
+// The workspace's flag words must be zero on entry; they are zero again when
+// the kernel ends.
+StreamK plan_streamk(const GemmArgs& a, ScaleMode scales, bool out_f32);
+int64_t streamk_workspace_bytes(const StreamK& sk);
+hipError_t launch_gemm_streamk(const GemmArgs& a, ScaleMode scales, bool out_f32, void* workspace,
+                               int64_t workspace_bytes, hipStream_t stream);
 
 hipError_t launch_diag_e4m3_census(uint32_t* min_bits, uint32_t* max_bits, unsigned long long* counts,
                                    hipStream_t stream);

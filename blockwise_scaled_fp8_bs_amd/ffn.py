@@ -76,7 +76,7 @@ class _GatedFFNFn(torch.autograd.Function):
         M = ab.shape[0]
         dev = ab.device
         dh = _b.bs_scaled_mm(qg, sg, qot[0], sot[0], _b.BS_SCALE_128X128, out_dtype=torch.bfloat16)
-        dwo = _b.bs_scaled_mm(qgt, sgt, qht, sht, _b.BS_SCALE_1X128, out_dtype=torch.bfloat16)
+        dwo = _b.bs_scaled_mm_ws(qgt, sgt, qht, sht, _b.BS_SCALE_1X128, out_dtype=torch.bfloat16)
         # [da | db] (the activation's backward) quantized in one pass over a, b, dh
         qd = torch.empty((M, 2 * H), dtype=torch.uint8, device=dev)
         sd = _b.empty_scales(2 * H // 128, M, dev)
@@ -87,7 +87,7 @@ class _GatedFFNFn(torch.autograd.Function):
         if ctx.needs_input_grad[0]:
             dx = _b.bs_scaled_mm(qd, sd, q12t[0], s12t[0], _b.BS_SCALE_128X128, out_dtype=torch.bfloat16)
         if ctx.needs_input_grad[1] or ctx.needs_input_grad[2]:
-            dw12 = _b.bs_scaled_mm(qdt, sdt, qxt, sxt, _b.BS_SCALE_1X128, out_dtype=torch.bfloat16)
+            dw12 = _b.bs_scaled_mm_ws(qdt, sdt, qxt, sxt, _b.BS_SCALE_1X128, out_dtype=torch.bfloat16)
             dw1, dw2 = dw12[:H], dw12[H:]
         return dx, dw1, dw2, dwo
 

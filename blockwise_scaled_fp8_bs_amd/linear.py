@@ -73,7 +73,7 @@ class _Float8BlockwiseLinearFn(torch.autograd.Function):
         if ctx.needs_input_grad[0]:
             dx = _b.bs_scaled_mm(qg, sg, qwt[0], swt[0], _b.BS_SCALE_128X128, out_dtype=torch.bfloat16)
         if ctx.needs_input_grad[1]:
-            dw = _b.bs_scaled_mm(qgt, sgt, qxt, sxt, _b.BS_SCALE_1X128, out_dtype=ctx.w_dtype)
+            dw = _b.bs_scaled_mm_ws(qgt, sgt, qxt, sxt, _b.BS_SCALE_1X128, out_dtype=ctx.w_dtype)
         return dx, dw
 
 

@@ -329,6 +329,46 @@ bs_status bs_scaled_mm(int64_t M, int64_t N, int64_t K,
                        hipStream_t stream);
 
 /*
+ * bs_scaled_mm_ws -- bs_scaled_mm with a caller-provided device workspace
+ * that lets the kernel balance a ragged last round of output tiles: when the
+ * tiles are not a multiple of the GPU's resident workgroups, the K blocks of
+ * the last round's tiles are divided evenly over all workgroups ("stream-K"),
+ * and each split tile is summed by the workgroup holding its first K blocks
+ * from the fp32 partial tiles the others leave in the workspace (in a fixed
+ * order, so results are reproducible run to run; they may differ from
+ * bs_scaled_mm's in the last bits, since the K blocks of a split tile are
+ * added in a different grouping -- both are within the recipe's tolerance).
+ * Same result definition as bs_scaled_mm (pages: as there; the wgrad GEMM of
+ * the FFN layers leaves part of the GPU idle in its last round of tiles).
+ *
+ *   All arguments as bs_scaled_mm, plus
+ *   workspace        DEVICE memory, 256-byte aligned, owned by the caller;
+ *                    its first 4096 bytes must be zero before the first call
+ *                    that uses it (e.g. hipMemset once); every call leaves
+ *                    them zero again.  NULL with workspace_bytes == 0 is
+ *                    allowed.
+ *   workspace_bytes  its size; bs_scaled_mm_workspace_bytes() gives what a
+ *                    problem needs on the current device.  With less (or for
+ *                    problems whose tiles fill every round) the call runs as
+ *                    bs_scaled_mm and does not touch the workspace.
+ * Calls that share a workspace must not overlap in time (use one stream, or
+ * one workspace per stream).  Errors as bs_scaled_mm, plus BS_ERR_ALIGN for a
+ * misaligned workspace and BS_ERR_NULL for a NULL one with nonzero size.
+ */
+bs_status bs_scaled_mm_ws(int64_t M, int64_t N, int64_t K,
+                          const uint8_t* a, int64_t lda, const float* sa, int64_t ld_sa,
+                          bs_scale_kind a_kind,
+                          const uint8_t* b, int64_t ldb, const float* sb, int64_t ld_sb,
+                          bs_scale_kind b_kind,
+                          void* d, int64_t ldd, bs_dtype d_dtype,
+                          void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes bs_scaled_mm_ws uses for this problem on the current
+ * device (0: the problem's tiles fill every round, no split).  Invalid
+ * arguments also give 0. */
+int64_t bs_scaled_mm_workspace_bytes(int64_t M, int64_t N, int64_t K, bs_scale_kind b_kind, bs_dtype d_dtype);
+
+/*
  * bs_grouped_scaled_mm -- the MoE form of bs_scaled_mm (pages: prototype page,
  * description, which lists grouped forward and backward GEMMs for MoE;
  * "[mxfp8 moe training] ...", microbenchmark table, shapes (M, N, K, G)).

@@ -24,7 +24,7 @@ PU = 0x10004  # a fake misaligned address
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:bs_status|const char\*)\s+(bs_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^(?:bs_status|const char\*|int64_t)\s+(bs_\w+)\s*\(", text, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -130,6 +130,41 @@ def test_scaled_mm_validation(lib, kw, code, frag):
 
 def test_scaled_mm_empty_is_ok(lib):
     assert _mm(lib, M=0) == OK
+
+
+def _mm_ws(lib, ws=P * 16, ws_bytes=1 << 20, **kw):
+    a = dict(M=256, N=256, K=512, a=P, lda=512, sa=P, ld_sa=256, a_kind=4, b=P, ldb=512, sb=P, ld_sb=4,
+             b_kind=5, d=P, ldd=256, dt=0)
+    a.update(kw)
+    return lib.bs_scaled_mm_ws(a["M"], a["N"], a["K"], a["a"], a["lda"], a["sa"], a["ld_sa"], a["a_kind"], a["b"],
+                               a["ldb"], a["sb"], a["ld_sb"], a["b_kind"], a["d"], a["ldd"], a["dt"], ws, ws_bytes,
+                               None)
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(ws=None), NULL, "workspace is NULL"),
+    (dict(ws=P + 16), ALIGN, "256-byte aligned"),
+    (dict(ws_bytes=-1), LAYOUT, "workspace_bytes"),
+    (dict(lda=256), LAYOUT, "row-major [M, K]"),
+    (dict(a_kind=5), MODE, "a_kind"),
+])
+def test_scaled_mm_ws_validation(lib, kw, code, frag):
+    assert _mm_ws(lib, **kw) == code
+    assert frag in lib.bs_last_error().decode()
+
+
+def test_scaled_mm_ws_empty_is_ok(lib):
+    assert _mm_ws(lib, M=0) == OK
+    assert _mm_ws(lib, M=0, ws=None, ws_bytes=0) == OK
+
+
+def test_workspace_query_is_zero_for_invalid_problems(lib):
+    f = lib.bs_scaled_mm_workspace_bytes
+    assert f(0, 256, 512, 4, 0) == 0
+    assert f(256, 200, 512, 4, 0) == 0     # N not a multiple of 128
+    assert f(256, 256, 500, 4, 0) == 0     # K not a multiple of 128
+    assert f(256, 256, 512, 7, 0) == 0     # unknown scale kind
+    assert f(256, 256, 512, 4, 0) >= 0
 
 
 def test_grouped_validation(lib):

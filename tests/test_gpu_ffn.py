@@ -84,7 +84,7 @@ def test_gated_ffn_is_exactly_its_kernel_calls():
 
     qg, sg, qgt, sgt = _q1(dy)
     dh = bs.bs_scaled_mm(qg, sg, qot, sot, bs.BS_SCALE_128X128)
-    dwo_ref = bs.bs_scaled_mm(qgt, sgt, qht, sht, bs.BS_SCALE_1X128)
+    dwo_ref = bs.bs_scaled_mm_ws(qgt, sgt, qht, sht, bs.BS_SCALE_1X128)
     dab = torch.empty((M, 2 * H), dtype=torch.bfloat16, device="cuda")
     qd = torch.empty((M, 2 * H), dtype=torch.uint8, device="cuda")
     sd = bs.empty_scales(2 * H // 128, M, "cuda")
@@ -99,7 +99,7 @@ def test_gated_ffn_is_exactly_its_kernel_calls():
     q12t = torch.cat([q1t, q2t], 1)
     s12t = torch.cat([s1t, s2t], 0)
     dx_ref = bs.bs_scaled_mm(qd, sd, q12t.contiguous(), s12t.contiguous(), bs.BS_SCALE_128X128)
-    dw12_ref = bs.bs_scaled_mm(qdt, sdt, qxt, sxt, bs.BS_SCALE_1X128)
+    dw12_ref = bs.bs_scaled_mm_ws(qdt, sdt, qxt, sxt, bs.BS_SCALE_1X128)
     torch.cuda.synchronize()
     assert torch.equal(wo.grad, dwo_ref)
     assert torch.equal(x.grad, dx_ref)

@@ -61,7 +61,7 @@ def test_layer_is_exactly_its_kernel_calls():
     swt = torch.empty((1, N // 128, 4), dtype=torch.float32, device="cuda")
     bs.bs_quant_3d_colwise(wd[None], qwt, swt)
     dx_ref = bs.bs_scaled_mm(qg, sg, qwt[0], swt[0], bs.BS_SCALE_128X128)
-    dw_ref = bs.bs_scaled_mm(qgt, sgt, qxt, sxt, bs.BS_SCALE_1X128)
+    dw_ref = bs.bs_scaled_mm_ws(qgt, sgt, qxt, sxt, bs.BS_SCALE_1X128)
     torch.cuda.synchronize()
     assert torch.equal(y, y_ref)
     assert torch.equal(x.grad, dx_ref)
