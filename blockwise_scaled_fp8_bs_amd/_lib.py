@@ -29,6 +29,8 @@ SIGNATURES = {
     "bs_scaled_mm_ws": (_E, [_I64, _I64, _I64, _P, _I64, _P, _I64, _E, _P, _I64, _P, _I64, _E, _P, _I64, _E, _P,
                              _I64, _P]),
     "bs_scaled_mm_workspace_bytes": (_I64, [_I64, _I64, _I64, _E, _E]),
+    "bs_scaled_mm_noalloc": (_E, [_I64, _I64, _I64, _P, _I64, _P, _I64, _E, _P, _I64, _P, _I64, _E, _P, _I64, _E,
+                                  _P]),
     "bs_grouped_scaled_mm": (_E, [_E, _I64, _I64, _I64, _I64, _P, _P, _I64, _P, _I64, _P, _I64, _I64, _P, _I64,
                                   _I64, _E, _P, _I64, _I64, _E, _P]),
     "bs_status_string": (ctypes.c_char_p, [_E]),

@@ -2,6 +2,7 @@
 // launch on the caller's stream.  Declarations and contracts: include/bs.h.
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/bs.h"
@@ -560,6 +561,76 @@ bs_status bs_scaled_mm_ws(int64_t M, int64_t N, int64_t K, const uint8_t* a, int
     return hip_status(bs::launch_gemm_streamk(g, b_kind == BS_SCALE_1X128 ? bs::kScale1x128 : bs::kScale128x128,
                                               d_dtype == BS_OUT_F32, workspace, workspace_bytes, stream),
                       fn);
+}
+
+}  // extern "C"
+
+// Device scratch of bs_scaled_mm_noalloc: the stream-K flag words (4 KiB)
+// and one 256 x 256 fp32 partial tile per split workgroup (at most 256 on a
+// 256-CU GPU), 64 MiB + 4 KiB per GPU, held until the process ends.  Host
+// code never uses the array's name as an address: each device's copy is
+// looked up once with hipGetSymbolAddress (scratch_on_device).
+static constexpr int64_t kScratchBytes = 4096 + (int64_t)256 * 256 * 256 * 4;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's scratch address (set up on the first call on the device,
+// with that device current).
+hipError_t scratch_on_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+bs_status bs_scaled_mm_noalloc(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const float* sa,
+                               int64_t ld_sa, bs_scale_kind a_kind, const uint8_t* b, int64_t ldb, const float* sb,
+                               int64_t ld_sb, bs_scale_kind b_kind, void* d, int64_t ldd, bs_dtype d_dtype,
+                               hipStream_t stream) {
+    static const char* fn = "bs_scaled_mm_noalloc";
+    REQUIRE(a_kind == BS_SCALE_1X128, BS_ERR_MODE, "a_kind=%d: A takes 1x128 scales (BS_SCALE_1X128 = 4)",
+            (int)a_kind);
+    bs_status st = check_gemm_common(fn, M, N, K, a, lda, sa, ld_sa, b, ldb, sb, ld_sb, b_kind, d, ldd, d_dtype);
+    if (st != BS_OK) return st;
+    REQUIRE(ld_sa >= M, BS_ERR_LAYOUT, "ld_sa=%lld < M=%lld: sa is K-major [K/128][ld_sa >= M]",
+            (long long)ld_sa, (long long)M);
+    const int64_t nrows_sb = b_kind == BS_SCALE_1X128 ? N : N / 128;
+    REQUIRE(ld_sb >= nrows_sb, BS_ERR_LAYOUT, "ld_sb=%lld < %lld: sb is K-major [K/128][ld_sb >= %s]",
+            (long long)ld_sb, (long long)nrows_sb, b_kind == BS_SCALE_1X128 ? "N" : "N/128");
+    if (M == 0 || N == 0) return ok();
+    const bs::GemmArgs g = dense_args(M, N, K, a, lda, sa, ld_sa, b, ldb, sb, ld_sb, d, ldd);
+    const bs::ScaleMode sc = b_kind == BS_SCALE_1X128 ? bs::kScale1x128 : bs::kScale128x128;
+    const int64_t need = bs::streamk_workspace_bytes(bs::plan_streamk(g, sc, d_dtype == BS_OUT_F32));
+    REQUIRE(need <= kScratchBytes, BS_ERR_SHAPE,
+            "the split of this problem needs %lld bytes of scratch; the static scratch holds %lld "
+            "(use bs_scaled_mm_ws with a larger workspace)", (long long)need, (long long)kScratchBytes);
+    if (need == 0) return hip_status(bs::launch_gemm(g, bs::kDense, sc, d_dtype == BS_OUT_F32, stream), fn);
+    void* ws = nullptr;
+    hipError_t e = scratch_on_device(&ws);
+    if (e != hipSuccess) return fail(BS_ERR_HIP, fn, "device scratch lookup failed: %s", hipGetErrorString(e));
+    // the flag words must start at zero whatever the previous call left
+    e = bs::launch_zero_words(static_cast<uint32_t*>(ws), 1024, stream);
+    if (e != hipSuccess) return hip_status(e, fn);
+    return hip_status(bs::launch_gemm_streamk(g, sc, d_dtype == BS_OUT_F32, ws, kScratchBytes, stream), fn);
 }
 
 bs_status bs_grouped_scaled_mm(bs_group_mode mode, int64_t G, int64_t M, int64_t N, int64_t K,

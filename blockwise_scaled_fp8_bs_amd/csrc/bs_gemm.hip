@@ -956,6 +956,20 @@ hipError_t launch_gemm_streamk(const GemmArgs& a, ScaleMode scales, bool out_f32
                    : launch_grid(gemm_sk_kernel<false, false>, grid, g, stream);
 }
 
+namespace {
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+}  // namespace
+
+hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, stream, p,
+                       n);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmArgs& a, GroupKind kind, ScaleMode scales, bool out_f32, hipStream_t stream) {
     switch (kind) {
         case kDense: return launch_kind<kDense>(a, scales, out_f32, stream);

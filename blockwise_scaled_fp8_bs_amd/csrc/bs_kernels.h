@@ -122,6 +122,10 @@ int64_t streamk_workspace_bytes(const StreamK& sk);
 hipError_t launch_gemm_streamk(const GemmArgs& a, ScaleMode scales, bool out_f32, void* workspace,
                                int64_t workspace_bytes, hipStream_t stream);
 
+// Zero n 32-bit words on the stream with a kernel (graph-capturable, unlike
+// a memset node).
+hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream);
+
 hipError_t launch_diag_e4m3_census(uint32_t* min_bits, uint32_t* max_bits, unsigned long long* counts,
                                    hipStream_t stream);
 hipError_t launch_diag_division(unsigned long long* result, hipStream_t stream);

@@ -363,6 +363,29 @@ bs_status bs_scaled_mm_ws(int64_t M, int64_t N, int64_t K,
                           void* d, int64_t ldd, bs_dtype d_dtype,
                           void* workspace, int64_t workspace_bytes, hipStream_t stream);
 
+/*
+ * bs_scaled_mm_noalloc -- bs_scaled_mm_ws for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels, with the workspace
+ * replaced by a static device array of the library, 64 MiB + 4 KiB on each
+ * GPU the library runs on (held until the process ends).  The call makes no
+ * allocation of any kind; the caller passes inputs and outputs only.  Each
+ * call first zeroes the array's flag words with a small kernel on `stream`.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (different streams, or several threads) race -- issue them on
+ * one stream.  A problem whose split would need more than the array holds
+ * is rejected with BS_ERR_SHAPE (not on a 256-CU GPU, which needs at most
+ * 64 MiB + 4 KiB); problems that are not split run as bs_scaled_mm.
+ * Arguments, result and errors as bs_scaled_mm; BS_ERR_HIP if the device
+ * array cannot be located.
+ */
+bs_status bs_scaled_mm_noalloc(int64_t M, int64_t N, int64_t K,
+                               const uint8_t* a, int64_t lda, const float* sa, int64_t ld_sa,
+                               bs_scale_kind a_kind,
+                               const uint8_t* b, int64_t ldb, const float* sb, int64_t ld_sb,
+                               bs_scale_kind b_kind,
+                               void* d, int64_t ldd, bs_dtype d_dtype, hipStream_t stream);
+
 /* Workspace bytes bs_scaled_mm_ws uses for this problem on the current
  * device (0: the problem's tiles fill every round, no split).  Invalid
  * arguments also give 0. */
