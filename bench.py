@@ -654,6 +654,32 @@ def main():
         extra[x] = {"ms_per_step": round(msx, 4), "value": round(sm["value"], 1), "unit": "TFLOP/s",
                     "gemm_tflops": round(sm["gemm_tflops"], 1), "quant_gbs": round(sm["quant_gbs"], 1),
                     "kernels": {k: {kk: vv for kk, vv in v.items() if kk != "work"} for k, v in pk.items()}}
+        if not args.no_fusion:
+            # The forward GEMM's epilogue quantizing its own bf16 output for
+            # the next layer (1x128 rows + transposed columns), against the
+            # GEMM followed by the separate quantizer pass over D.
+            Mx, Nx = wx.M, wx.N
+            qr_ = torch.empty((Mx, Nx), dtype=torch.uint8, device="cuda")
+            sr_ = bs.empty_scales(Nx // 128, Mx, "cuda")
+            qc_ = torch.empty((Nx, Mx), dtype=torch.uint8, device="cuda")
+            sc_ = bs.empty_scales(Mx // 128, Nx, "cuda")
+            fargs = (sx.qa, sx.sa, sx.qw, sx.sw, bs.BS_SCALE_128X128)
+
+            def sep():
+                bs.bs_scaled_mm(*fargs, out=sx.out)
+                bs.bs_quant_1x128(sx.out, qr_, sr_, qc_, sc_)
+
+            def fused_q():
+                bs.bs_scaled_mm_quant(*fargs, q_row=qr_, s_row=sr_, q_col=qc_, s_col=sc_)
+
+            def fused_qd():
+                bs.bs_scaled_mm_quant(*fargs, out=sx.out, q_row=qr_, s_row=sr_, q_col=qc_, s_col=sc_)
+
+            s_ms, q_ms, qd_ms = median_ms(sep), median_ms(fused_q), median_ms(fused_qd)
+            extra[x]["gemm_quant_epilogue"] = {
+                "separate_ms": round(s_ms, 4), "fused_ms": round(q_ms, 4), "fused_with_d_ms": round(qd_ms, 4),
+                "speedup": round(s_ms / q_ms, 3), "speedup_with_d": round(s_ms / qd_ms, 3)}
+            del qr_, sr_, qc_, sc_
         if not args.no_fusion and fusion is None:
             # Fusion next to the path: the FFN's gated activation h = silu(a) * b
             # quantized for the next layer (rows + transposed columns), fused in

@@ -26,6 +26,7 @@ from .binding import (  # noqa: F401
     bs_swiglu_bwd_quant_1x128,
     bs_swiglu_quant_1x128,
     bs_scaled_mm,
+    bs_scaled_mm_quant,
     bs_scaled_mm_workspace_bytes,
     bs_scaled_mm_ws,
     empty_mx_scales,

@@ -26,6 +26,8 @@ SIGNATURES = {
     "bs_quant_128x128_both": (_E, [_P, _I64, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P, _I64,
                                    _I64, _P]),
     "bs_scaled_mm": (_E, [_I64, _I64, _I64, _P, _I64, _P, _I64, _E, _P, _I64, _P, _I64, _E, _P, _I64, _E, _P]),
+    "bs_scaled_mm_quant": (_E, [_I64, _I64, _I64, _P, _I64, _P, _I64, _E, _P, _I64, _P, _I64, _E, _P, _I64,
+                                _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P]),
     "bs_scaled_mm_ws": (_E, [_I64, _I64, _I64, _P, _I64, _P, _I64, _E, _P, _I64, _P, _I64, _E, _P, _I64, _E, _P,
                              _I64, _P]),
     "bs_scaled_mm_workspace_bytes": (_I64, [_I64, _I64, _I64, _E, _E]),

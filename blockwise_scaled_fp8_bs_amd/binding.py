@@ -385,6 +385,42 @@ def bs_scaled_mm(a, sa, b, sb, b_kind, out=None, out_dtype=torch.bfloat16, strea
     return out
 
 
+def bs_scaled_mm_quant(a, sa, b, sb, b_kind, out=None, q_row=None, s_row=None, q_col=None, s_col=None,
+                       stream=None):
+    """D = A . B^T (bf16) whose epilogue also writes the 1x128 quantization of
+    D: q_row [M, N] uint8 with s_row [N/128, >= M], and/or q_col [N, M] with
+    s_col [M/128, >= N] -- exactly what bs_quant_1x128(D, ...) writes.
+    ``out`` (bf16 [M, N]) is optional; returns it (or None)."""
+    _mat(a, "a", torch.uint8)
+    _mat(b, "b", torch.uint8)
+    M, K = a.shape
+    N, Kb = b.shape
+    _require(K == Kb, f"a is [M, {K}] but b is [N, {Kb}]: both must be contiguous along the same K")
+    ld_sa = _scale(sa, "sa", K // 128, M)
+    ld_sb = _scale(sb, "sb", K // 128, N if b_kind == BS_SCALE_1X128 else (N + 127) // 128)
+    args = [M, N, K, _ptr(a), _ld(a), _ptr(sa), ld_sa, BS_SCALE_1X128, _ptr(b), _ld(b), _ptr(sb), ld_sb, b_kind]
+    if out is not None:
+        _mat(out, "out", torch.bfloat16)
+        _require(tuple(out.shape) == (M, N), f"out must be [{M}, {N}]")
+        args += [_ptr(out), _ld(out)]
+    else:
+        args += [None, N]
+    if q_row is not None or s_row is not None:
+        _mat(q_row, "q_row", torch.uint8)
+        _require(tuple(q_row.shape) == (M, N), f"q_row must be [{M}, {N}]")
+        args += [_ptr(q_row), _ld(q_row), _ptr(s_row), _scale(s_row, "s_row", N // 128, M)]
+    else:
+        args += [None, 0, None, 0]
+    if q_col is not None or s_col is not None:
+        _mat(q_col, "q_col", torch.uint8)
+        _require(tuple(q_col.shape) == (N, M), f"q_col must be the transpose [{N}, {M}]")
+        args += [_ptr(q_col), _ld(q_col), _ptr(s_col), _scale(s_col, "s_col", M // 128, N)]
+    else:
+        args += [None, 0, None, 0]
+    _check(_lib.load().bs_scaled_mm_quant(*args, _stream(stream)), "bs_scaled_mm_quant")
+    return out
+
+
 def bs_scaled_mm_workspace_bytes(M, N, K, b_kind, out_dtype=torch.bfloat16):
     """Workspace bytes bs_scaled_mm_ws uses for this problem on the current device (0: no split)."""
     dt = {torch.bfloat16: BS_OUT_BF16, torch.float32: BS_OUT_F32}.get(out_dtype)
@@ -396,24 +432,23 @@ _WORKSPACES = {}
 
 
 def streamk_workspace(nbytes, device=None):
-    """A zero-initialised device workspace of at least ``nbytes`` for
-    bs_scaled_mm_ws, cached per device and grown on demand (torch owns the
-    memory).  Calls that share it must not overlap in time: use it from one
-    stream."""
+    """A device workspace of at least ``nbytes`` for bs_scaled_mm_ws, cached
+    per device and grown on demand (torch owns the memory).  Calls that share
+    it must not overlap in time: use it from one stream."""
     device = torch.device("cuda" if device is None else device)
     if device.index is None:
         device = torch.device(device.type, torch.cuda.current_device())
     ws = _WORKSPACES.get(device)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(nbytes, 4096), dtype=torch.uint8, device=device)
         _WORKSPACES[device] = ws
     return ws
 
 
 def bs_scaled_mm_ws(a, sa, b, sb, b_kind, workspace=None, out=None, out_dtype=torch.bfloat16, stream=None):
     """bs_scaled_mm with a device workspace (uint8 GPU tensor, 256-byte
-    aligned, first 4096 bytes zero before first use) that lets the kernel
-    split a ragged last round of tiles along K; see include/bs.h.  With
+    aligned) that lets the kernel split a ragged last round of tiles along
+    K; see include/bs.h.  With
     ``workspace=None`` the per-device cached workspace (streamk_workspace)
     sized for this problem is used."""
     _mat(a, "a", torch.uint8)

@@ -55,7 +55,7 @@ def build(verbose=False):
     with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
         outs = list(ex.map(_run, cmds))
     tmp = LIB + ".tmp"
-    outs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]))
+    outs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp]))
     os.replace(tmp, LIB)
     if verbose:
         for o in outs:

@@ -529,6 +529,64 @@ bs::GemmArgs dense_args(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64
 
 }  // namespace
 
+bs_status bs_scaled_mm_quant(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const float* sa,
+                             int64_t ld_sa, bs_scale_kind a_kind, const uint8_t* b, int64_t ldb, const float* sb,
+                             int64_t ld_sb, bs_scale_kind b_kind, uint16_t* d, int64_t ldd, uint8_t* q_row,
+                             int64_t ld_qr, float* s_row, int64_t ld_sr, uint8_t* q_col, int64_t ld_qc, float* s_col,
+                             int64_t ld_sc, hipStream_t stream) {
+    static const char* fn = "bs_scaled_mm_quant";
+    const bool row = q_row || s_row, col = q_col || s_col;
+    const bool empty = M == 0 || N == 0;
+    REQUIRE(a_kind == BS_SCALE_1X128, BS_ERR_MODE, "a_kind=%d: A takes 1x128 scales (BS_SCALE_1X128 = 4)",
+            (int)a_kind);
+    REQUIRE(!row || (q_row && s_row) || empty, BS_ERR_NULL, "q_row and s_row must both be set or both NULL");
+    REQUIRE(!col || (q_col && s_col) || empty, BS_ERR_NULL, "q_col and s_col must both be set or both NULL");
+    REQUIRE(d || row || col || empty, BS_ERR_NULL, "no output requested (d, q_row/s_row and q_col/s_col all NULL)");
+    // d is checked as bs_scaled_mm's bf16 output when given (a stand-in pointer otherwise)
+    bs_status st = check_gemm_common(fn, M, N, K, a, lda, sa, ld_sa, b, ldb, sb, ld_sb, b_kind,
+                                     d ? static_cast<void*>(d) : reinterpret_cast<void*>(16), d ? ldd : N,
+                                     BS_OUT_BF16);
+    if (st != BS_OK) return st;
+    REQUIRE(ld_sa >= M, BS_ERR_LAYOUT, "ld_sa=%lld < M=%lld: sa is K-major [K/128][ld_sa >= M]",
+            (long long)ld_sa, (long long)M);
+    const int64_t nrows_sb = b_kind == BS_SCALE_1X128 ? N : N / 128;
+    REQUIRE(ld_sb >= nrows_sb, BS_ERR_LAYOUT, "ld_sb=%lld < %lld: sb is K-major [K/128][ld_sb >= %s]",
+            (long long)ld_sb, (long long)nrows_sb, b_kind == BS_SCALE_1X128 ? "N" : "N/128");
+    REQUIRE(!col || M % 128 == 0, BS_ERR_SHAPE,
+            "M=%lld must be a multiple of 128 for the column output (128-row blocks)", (long long)M);
+    if (row) {
+        REQUIRE(ld_qr >= N && ld_qr < kMaxLd, BS_ERR_LAYOUT, "ld_qr=%lld must be >= N=%lld (q_row is [M, N]) and < 2^22",
+                (long long)ld_qr, (long long)N);
+        REQUIRE(ld_sr >= M && ld_sr % 4 == 0, BS_ERR_LAYOUT,
+                "ld_sr=%lld must be >= M=%lld and a multiple of 4 (s_row is K-major [N/128][ld_sr])",
+                (long long)ld_sr, (long long)M);
+        REQUIRE(aligned16(q_row) && ld_qr % 16 == 0 && aligned16(s_row), BS_ERR_ALIGN,
+                "q_row and s_row must be 16-byte aligned with ld_qr %% 16 == 0");
+    }
+    if (col) {
+        REQUIRE(ld_qc >= M && ld_qc < kMaxLd, BS_ERR_LAYOUT,
+                "ld_qc=%lld must be >= M=%lld (q_col is the transpose [N, M]) and < 2^22", (long long)ld_qc,
+                (long long)M);
+        REQUIRE(ld_sc >= N && ld_sc % 4 == 0, BS_ERR_LAYOUT,
+                "ld_sc=%lld must be >= N=%lld and a multiple of 4 (s_col is K-major [M/128][ld_sc])",
+                (long long)ld_sc, (long long)N);
+        REQUIRE(aligned16(q_col) && ld_qc % 16 == 0 && aligned16(s_col), BS_ERR_ALIGN,
+                "q_col and s_col must be 16-byte aligned with ld_qc %% 16 == 0");
+    }
+    if (empty) return ok();
+    bs::GemmArgs g = dense_args(M, N, K, a, lda, sa, ld_sa, b, ldb, sb, ld_sb, d, ldd);
+    g.q_row = row ? q_row : nullptr;
+    g.ld_qr = ld_qr;
+    g.s_row = row ? s_row : nullptr;
+    g.ld_sr = ld_sr;
+    g.q_col = col ? q_col : nullptr;
+    g.ld_qc = ld_qc;
+    g.s_col = col ? s_col : nullptr;
+    g.ld_sc = ld_sc;
+    return hip_status(
+        bs::launch_gemm_quant(g, b_kind == BS_SCALE_1X128 ? bs::kScale1x128 : bs::kScale128x128, stream), fn);
+}
+
 int64_t bs_scaled_mm_workspace_bytes(int64_t M, int64_t N, int64_t K, bs_scale_kind b_kind, bs_dtype d_dtype) {
     if (M <= 0 || N <= 0 || K <= 0 || N % 128 || K % 128) return 0;
     if (b_kind != BS_SCALE_1X128 && b_kind != BS_SCALE_128X128) return 0;
@@ -565,12 +623,13 @@ bs_status bs_scaled_mm_ws(int64_t M, int64_t N, int64_t K, const uint8_t* a, int
 
 }  // extern "C"
 
-// Device scratch of bs_scaled_mm_noalloc: the stream-K flag words (4 KiB)
-// and one 256 x 256 fp32 partial tile per split workgroup (at most 256 on a
-// 256-CU GPU), 64 MiB + 4 KiB per GPU, held until the process ends.  Host
-// code never uses the array's name as an address: each device's copy is
-// looked up once with hipGetSymbolAddress (scratch_on_device).
-static constexpr int64_t kScratchBytes = 4096 + (int64_t)256 * 256 * 256 * 4;
+// Device scratch of bs_scaled_mm_noalloc: one 256 x 256 fp32 partial tile
+// per stream-K piece -- split tiles + splitting workgroups, at most
+// 192 + 256 = 448 on a 256-CU GPU (a split last round is at most 3/4 full)
+// -- 112 MiB per GPU, held until the process ends.  Host code never uses the
+// array's name as an address: each device's copy is looked up once with
+// hipGetSymbolAddress (scratch_on_device).
+static constexpr int64_t kScratchBytes = (int64_t)448 * 256 * 256 * 4;
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
@@ -627,9 +686,6 @@ bs_status bs_scaled_mm_noalloc(int64_t M, int64_t N, int64_t K, const uint8_t* a
     void* ws = nullptr;
     hipError_t e = scratch_on_device(&ws);
     if (e != hipSuccess) return fail(BS_ERR_HIP, fn, "device scratch lookup failed: %s", hipGetErrorString(e));
-    // the flag words must start at zero whatever the previous call left
-    e = bs::launch_zero_words(static_cast<uint32_t*>(ws), 1024, stream);
-    if (e != hipSuccess) return hip_status(e, fn);
     return hip_status(bs::launch_gemm_streamk(g, sc, d_dtype == BS_OUT_F32, ws, kScratchBytes, stream), fn);
 }
 

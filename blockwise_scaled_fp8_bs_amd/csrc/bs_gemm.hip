@@ -39,6 +39,7 @@
 //    accumulates straight into the fp32 tile and there is no VALU fold.
 //    The scale bytes of a K block (4 chunks x 256 rows per operand, 1 KiB)
 //    ride along with its operand tiles.
+#include "bs_device.h"
 #include "bs_kernels.h"
 
 namespace bs {
@@ -84,6 +85,8 @@ struct __attribute__((aligned(16))) Smem {
     int32_t slice_start[8 * kMaxSlicedGroups + 1];
     int32_t g_start[kMaxSlicedGroups], g_end[kMaxSlicedGroups], g_rows[kMaxSlicedGroups];
     int32_t wave_sum[NT / 64];
+    // quantizing epilogue: each wave's half-row amaxes [wm][wn][i][lane % 16]
+    float row_amax[2][WAVES_N][TM][16];
 };
 
 // Read-only views of the GROUP_M slice tables (LDS).
@@ -116,69 +119,76 @@ struct Tile {
     int32_t n0;
     int32_t kb0, kb1;    // K blocks [kb0, kb1)
     int32_t g;           // group: whose B (GROUP_M) or which D (GROUP_K)
-    int32_t role;        // stream-K: 0 whole tile, 1 later K blocks (partial for the owner), 2 owner
-    int32_t sk_last;     // owner: the last workgroup holding a part of this tile
+    int32_t role;        // stream-K: 0 whole tile, 1 a piece (its partial goes to the workspace)
+    int32_t sk_last;     // stream-K piece: its workspace slot
 };
 
-// Stream-K work item q of this workgroup (dense problems): first the whole
-// tiles q * grid + blockIdx.x of the leading rounds, then the pieces of the
-// split tiles that fall into this workgroup's share [i0, i1) of their K
-// iterations, in order.  Shares are dealt by a virtual index v that gives the
-// workgroups of one XCD consecutive shares (so an XCD works on a few
-// neighbouring tiles and shares their operand panels in its L2).  A piece
-// that starts a tile's K range is its owner: it adds the partial tiles of
-// the later pieces (virtual workgroups v + 1 .. sk_last, each of which has
-// that piece as its first) before storing D.
-__device__ __forceinline__ int64_t sk_virtual(const GemmArgs& p) {
-    return (int64_t)blockIdx.x < p.sk_wgs ? xcd_remap(blockIdx.x, p.sk_wgs) : (int64_t)blockIdx.x;
+// Stream-K split of a dense problem.  The K iterations of the split tiles
+// (the ragged last round) are divided evenly over sk_wgs workgroups, whose
+// shares are dealt by a virtual index v that gives the workgroups of one XCD
+// consecutive shares (an XCD then works on a few neighbouring tiles and
+// shares their operand panels in its L2).  Work item q of a workgroup: first
+// the whole tiles q * grid + blockIdx.x of the leading rounds, then the
+// pieces of its share, one per split tile it touches, in order.  Every piece
+// leaves its fp32 partial tile in slot v + t of the workspace (tile t, share
+// v: the pairs (t, v) of all pieces form a staircase, so v + t is unique);
+// a second kernel adds each tile's partials in share order and writes D.
+struct SkPlan {
+    int32_t v;          // virtual workgroup index (share order)
+    int32_t dp_rounds;  // rounds of whole tiles
+    int32_t nkb;        // K blocks per tile
+    int32_t t0;         // first split tile of this share
+    int32_t i0, i1;     // this share of the split tiles' K iterations (i1 <= i0: none)
+};
+
+// Wave-uniform values in scalar registers.
+__device__ __forceinline__ int32_t uni(int64_t x) { return __builtin_amdgcn_readfirstlane((int32_t)x); }
+
+__device__ __forceinline__ SkPlan sk_plan(const GemmArgs& p) {
+    SkPlan s;
+    const int64_t P = gridDim.x, b = blockIdx.x;
+    s.v = uni(b < p.sk_wgs ? xcd_remap(b, p.sk_wgs) : b);
+    s.dp_rounds = uni(p.sk_dp_tiles / P);
+    s.nkb = uni(p.K / BK);
+    const int64_t I = p.sk_tiles * (int64_t)s.nkb;
+    if (s.v < p.sk_wgs) {
+        s.i0 = uni(s.v * I / p.sk_wgs);
+        s.i1 = uni((s.v + 1) * I / p.sk_wgs);
+    } else {
+        s.i0 = s.i1 = 0;
+    }
+    s.t0 = uni(s.i0 / s.nkb);
+    return s;
 }
 
-__device__ __forceinline__ bool sk_has_work(const GemmArgs& p, int64_t q) {
-    const int64_t P = gridDim.x, w = sk_virtual(p);
-    const int64_t dp_rounds = p.sk_dp_tiles / P;
-    if (q < dp_rounds) return true;
-    if (w >= p.sk_wgs) return false;
-    const int64_t nkb = p.K / BK, I = p.sk_tiles * nkb;
-    const int64_t i0 = w * I / p.sk_wgs, i1 = (w + 1) * I / p.sk_wgs;
-    return (i0 / nkb + (q - dp_rounds)) * nkb < i1;
+__device__ __forceinline__ bool sk_has_work(const SkPlan& s, int64_t q) {
+    if (q < s.dp_rounds) return true;
+    return (s.t0 + (q - s.dp_rounds)) * (int64_t)s.nkb < s.i1;
 }
 
-__device__ __forceinline__ bool sk_work(const GemmArgs& p, int64_t q, Tile& t) {
-    const int64_t P = gridDim.x, w = sk_virtual(p);
-    const int64_t nkb = p.K / BK;
-    const int64_t dp_rounds = p.sk_dp_tiles / P;
+__device__ __forceinline__ void sk_work(const GemmArgs& p, const SkPlan& s, int64_t q, Tile& t) {
     int64_t L;
     t.g = 0;
     t.role = 0;
     t.sk_last = 0;
     t.m_end = (int32_t)p.M;
-    if (q < dp_rounds) {
-        L = xcd_remap(q * P + blockIdx.x, p.sk_dp_tiles);
+    if (q < s.dp_rounds) {
+        L = xcd_remap(q * gridDim.x + blockIdx.x, p.sk_dp_tiles);
         t.kb0 = 0;
-        t.kb1 = (int32_t)nkb;
+        t.kb1 = s.nkb;
     } else {
-        if (w >= p.sk_wgs) return false;
-        const int64_t I = p.sk_tiles * nkb;
-        const int64_t i0 = w * I / p.sk_wgs, i1 = (w + 1) * I / p.sk_wgs;
-        const int64_t tt = i0 / nkb + (q - dp_rounds);
-        const int64_t s = i0 > tt * nkb ? i0 : tt * nkb;
-        const int64_t e = i1 < (tt + 1) * nkb ? i1 : (tt + 1) * nkb;
-        if (s >= e) return false;
+        const int32_t tt = s.t0 + (int32_t)(q - s.dp_rounds);
+        const int32_t lo = tt * s.nkb, hi = lo + s.nkb;
         L = p.sk_dp_tiles + tt;
-        t.kb0 = (int32_t)(s - tt * nkb);
-        t.kb1 = (int32_t)(e - tt * nkb);
-        if (t.kb0 > 0) {
-            t.role = 1;
-        } else if (t.kb1 < nkb) {
-            t.role = 2;
-            t.sk_last = (int32_t)(((tt + 1) * nkb * p.sk_wgs - 1) / I);
-        }
+        t.kb0 = (s.i0 > lo ? s.i0 : lo) - lo;
+        t.kb1 = (s.i1 < hi ? s.i1 : hi) - lo;
+        t.role = 1;
+        t.sk_last = s.v + tt;  // the piece's slot
     }
     int64_t tm, tn;
     grouped_order(L, p.tiles_m, p.tiles_n, tm, tn);
-    t.m0 = (int32_t)(tm * BM);
-    t.n0 = (int32_t)(tn * BN);
-    return true;
+    t.m0 = uni(tm * BM);
+    t.n0 = uni(tn * BN);
 }
 
 // Number of tiles; for GROUP_M also the tile rows summed over the groups
@@ -367,7 +377,125 @@ __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" :
 // lane offsets.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-template <int KIND, int SC, bool OUT_F32, bool SK = false>
+// Quantizing epilogue: the wave's 128 x 64 block of the output as bf16 (hb:
+// two values per word, columns 4 lg + {0, 1} and {2, 3} of MFMA tile (i, j),
+// the rounding the bf16 output gets), quantized in 1x128 blocks exactly as
+// bs_quant_1x128 quantizes a bf16 tensor.  The packed form halves the
+// registers the epilogue holds, which keeps the K loop free of spills.
+//  * rows: a block is 128 columns of one row, held by a pair of waves (wn,
+//    wn ^ 1); each lane reduces its 16 values, the 4 lanes of a row exchange
+//    maxima by shuffles, the pair through LDS.  Codes are staged in the
+//    wave's 8 KiB of the free LDS stage ([row][64 B], 16-byte chunks XOR-ed
+//    with row bits 2..3: conflict-free) and stored as whole 16-byte chunks;
+//  * columns: a block is the wave's 128 rows of one column: each lane
+//    reduces its 8 values, the 16 lanes of a DPP row hold one column's rows.
+//    Each lane encodes 4 columns of one row per dword; a 4 x 4 byte
+//    transpose across the lanes of a quad (two DPP exchanges, two byte
+//    permutes) turns them into 4 rows of one column, staged as [col][128 B]
+//    (16-byte chunks XOR-ed with column bits 1..3) and stored transposed.
+__device__ __forceinline__ float hb_val(const uint32_t (&hb)[TM][TN][2], int i, int j, int r) {
+    return (r & 1) ? bf16_hi(hb[i][j][r >> 1]) : bf16_lo(hb[i][j][r >> 1]);
+}
+
+// The lane index passed through an opaque move: address arithmetic derived
+// from it is then computed where it is used, in each tile's epilogue,
+// instead of being hoisted out of the tile loop and held (and spilled) across
+// the K loop.
+__device__ __forceinline__ int opaque_lane(int lane) {
+    int v;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "v"(lane));
+    return v;
+}
+
+__device__ __forceinline__ void quant_epilogue(const GemmArgs& p, const uint32_t (&hb)[TM][TN][2], uint8_t* stq,
+                                               float (*row_amax)[WAVES_N][TM][16], int64_t m_wave, int64_t m_end,
+                                               int64_t n_wave, int wm, int wn, int lane_in) {
+    const int lane = opaque_lane(lane_in);
+    const int lr = lane & 15, lg = lane >> 4;
+    const bool n_ok = n_wave < p.N;  // N % 128 == 0: a wave pair is wholly in or out
+    if (p.q_row) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            float m = 0.f;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(hb_val(hb, i, j, r)));
+            m = fmaxf(m, __shfl_xor(m, 16));
+            m = fmaxf(m, __shfl_xor(m, 32));
+            if (lg == 0) row_amax[wm][wn][i][lr] = m;
+        }
+        __syncthreads();
+        const int64_t scol = (n_wave / 128) * p.ld_sr;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const Scale sc = block_scale(fmaxf(row_amax[wm][wn][i][lr], row_amax[wm][wn ^ 1][i][lr]));
+            const int row = 16 * i + lr;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const uint32_t x = encode4(div_by_scale(hb_val(hb, i, j, 0), sc), div_by_scale(hb_val(hb, i, j, 1), sc),
+                                           div_by_scale(hb_val(hb, i, j, 2), sc), div_by_scale(hb_val(hb, i, j, 3), sc));
+                *reinterpret_cast<uint32_t*>(stq + row * 64 + ((j ^ ((row >> 2) & 3)) * 16) + 4 * lg) = x;
+            }
+            if (n_ok && (wn & 1) == 0 && lg == 0 && m_wave + row < m_end) p.s_row[scol + m_wave + row] = sc.s;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // other lanes' staging writes
+        if (n_ok) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int row = q * 16 + (lane >> 2), c = lane & 3;
+                const uint4 v = *reinterpret_cast<const uint4*>(stq + row * 64 + ((c ^ ((row >> 2) & 3)) * 16));
+                if (m_wave + row < m_end)
+                    *reinterpret_cast<uint4*>(p.q_row + (m_wave + row) * p.ld_qr + n_wave + c * 16) = v;
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // staging reads done before reuse
+    }
+    if (p.q_col && n_ok && m_wave < m_end) {  // M % 128 == 0: the wave's 128 rows are all valid
+        const int t4 = lane & 3, q4 = (lane >> 2) & 3;
+        const uint32_t sel1 = (t4 & 1) ? 0x03070105u : 0x06020400u;
+        const uint32_t sel2 = (t4 & 2) ? 0x03020706u : 0x05040100u;
+        const int64_t srow = (m_wave / 128) * p.ld_sc + n_wave;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            Scale cs[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float m = 0.f;
+#pragma unroll
+                for (int i = 0; i < TM; ++i) m = fmaxf(m, fabsf(hb_val(hb, i, j, r)));
+                cs[r] = block_scale(__uint_as_float(row16_max(__float_as_uint(m))));
+            }
+            const int col = 16 * j + 4 * lg + t4;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const uint32_t x =
+                    encode4(div_by_scale(hb_val(hb, i, j, 0), cs[0]), div_by_scale(hb_val(hb, i, j, 1), cs[1]),
+                            div_by_scale(hb_val(hb, i, j, 2), cs[2]), div_by_scale(hb_val(hb, i, j, 3), cs[3]));
+                // x: columns 4 lg .. + 3 of row 16 i + lane % 16; after the
+                // transpose: rows 16 i + 4 q4 .. + 3 of column col
+                const uint32_t px = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
+                const uint32_t z = __builtin_amdgcn_perm(px, x, sel1);
+                const uint32_t pz = (uint32_t)__builtin_amdgcn_mov_dpp((int)z, 0x4E, 0xF, 0xF, false);
+                const uint32_t y = __builtin_amdgcn_perm(pz, z, sel2);
+                *reinterpret_cast<uint32_t*>(stq + col * 128 + 16 * (i ^ ((col >> 1) & 7)) + 4 * q4) = y;
+            }
+            if (lr == 0)
+                *reinterpret_cast<float4*>(p.s_col + srow + 16 * j + 4 * lg) =
+                    make_float4(cs[0].s, cs[1].s, cs[2].s, cs[3].s);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int col = k * 8 + (lane >> 3), c = lane & 7;
+            const uint4 v = *reinterpret_cast<const uint4*>(stq + col * 128 + 16 * (c ^ ((col >> 1) & 7)));
+            *reinterpret_cast<uint4*>(p.q_col + (n_wave + col) * p.ld_qc + m_wave + c * 16) = v;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+}
+
+template <int KIND, int SC, bool OUT_F32, bool SK = false, bool QEPI = false>
 __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
     __shared__ Smem sm;  // one per instantiation; each kernel below uses one
     constexpr bool B1X128 = SC == kScale1x128;
@@ -381,10 +509,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
     int64_t rows_total;
     const int64_t total = tile_total<KIND>(p, rows_total);
     int64_t idx = blockIdx.x;  // tile index (stream-K: work item counter q)
+    SkPlan skp{};
     if (SK) {
-        Tile t0;
+        skp = sk_plan(p);
         idx = 0;
-        if (!sk_work(p, 0, t0)) return;
+        if (!sk_has_work(skp, 0)) return;
     } else if (idx >= total) {
         return;
     }
@@ -576,7 +705,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
 
     Tile cur;
     if (SK)
-        sk_work(p, idx, cur);
+        sk_work(p, skp, idx, cur);
     else
         resolve_tile<KIND>(p, idx, total, rows_total, sm.group_by_rank, slices, cur);
     Operands ops = make_operands<KIND, SC>(p, cur);
@@ -591,13 +720,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
         // The next tile of this workgroup: its first K block is loaded
         // during the last K block of this one.
         const int64_t nidx = SK ? idx + 1 : idx + gridDim.x;
-        const bool has_next = SK ? sk_has_work(p, nidx) : nidx < total;
+        const bool has_next = SK ? sk_has_work(skp, nidx) : nidx < total;
         Tile nxt = cur;
         Operands nops = ops;
         bool next_resolved = false;
         auto load_next = [&](int stage) {
             if (SK)
-                sk_work(p, nidx, nxt);
+                sk_work(p, skp, nidx, nxt);
             else
                 resolve_tile<KIND>(p, nidx, total, rows_total, sm.group_by_rank, slices, nxt);
             nops = make_operands<KIND, SC>(p, nxt);
@@ -703,73 +832,65 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
             s ^= 1;
         }
 
-        // ---- stream-K: a piece after a tile's first K blocks leaves its
-        // partial tile (lane-major, as the registers hold it) in this
-        // workgroup's slot and raises its flag; the owner adds the partials of
-        // virtual workgroups v + 1 .. sk_last, in that order, and clears their
-        // flags ----
+        // ---- stream-K: a piece leaves its partial tile in its slot,
+        // lane-major as the registers hold it (the reduction kernel reads it
+        // back in the same layout) ----
         bool store_d = true;
-        // The slot is addressed through a buffer descriptor: lane offset in one
-        // VGPR, the MFMA tile's 1 KiB step as the uniform offset.  Partial
-        // tiles are written and read at device scope (cache policy SC1: the
-        // stores go through this XCD's L2 to memory, the loads fetch from
-        // there), so that no cache-wide write-back or invalidate is needed
-        // -- other workgroups on the same XCD keep their cached operands.
-        const int sk_voff = (w * TM * TN * 64 + lane) * 16;
-        constexpr int kDeviceScope = 16;  // SC1
-        const int sk_v = SK ? (int)sk_virtual(p) : 0;
         if (SK && cur.role == 1) {
+            const int sk_voff = (w * TM * TN * 64 + opaque_lane(lane)) * 16;
             const __amdgpu_buffer_rsrc_t slot = __builtin_amdgcn_make_buffer_rsrc(
-                p.sk_partial + (int64_t)sk_v * (BM * BN), (short)0, BM * BN * 4, 0x00020000);
+                p.sk_partial + (int64_t)cur.sk_last * (BM * BN), (short)0, BM * BN * 4, 0x00020000);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), slot, sk_voff,
-                                                           (i * TN + j) * 1024, kDeviceScope);
-            // every store of the partial has reached device scope before the
-            // flag is raised
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            if (t == 0) __hip_atomic_store(&p.sk_flag[sk_v], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                                           (i * TN + j) * 1024, 0);
             store_d = false;
-        } else if (SK && cur.role == 2) {
-            bool lost = false;
-            for (int c = sk_v + 1; c <= cur.sk_last; ++c) {
-                // the flag is raised by a workgroup that has already finished
-                // its piece (pieces are its first work after the whole tiles);
-                // the bound only guards against a workspace whose flags were
-                // not zero on entry
-                int n = 0;
-                while (__hip_atomic_load(&p.sk_flag[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u &&
-                       n < (1 << 22)) {
-                    __builtin_amdgcn_s_sleep(2);
-                    ++n;
-                }
-                lost = lost || n >= (1 << 22);
-                // the loads below are issued after the flag was seen set
-                asm volatile("" ::: "memory");
-                const __amdgpu_buffer_rsrc_t slot = __builtin_amdgcn_make_buffer_rsrc(
-                    p.sk_partial + (int64_t)c * (BM * BN), (short)0, BM * BN * 4, 0x00020000);
+        }
+
+        if (QEPI) {
+            // the quantized values are those of the bf16 output: pack them
+            // (round to nearest even) and let the fp32 tile go
+            uint32_t hb[TM][TN][2];
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        hb[i][j][h] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][2 * h]) |
+                                      ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][2 * h + 1]) << 16);
+            uint8_t* const stq = (w < 4 ? sm.a[s ^ 1] : sm.b[s ^ 1]) + (w & 3) * 8192;
+            quant_epilogue(p, hb, stq, sm.row_amax, (int64_t)cur.m0 + wm * WM, cur.m_end, (int64_t)cur.n0 + wn * WN,
+                           wm, wn, lane);
+            if (p.d) {
+                // D from the packed values, staged as the plain epilogue does
+                constexpr int PITCH = WN * 2 + 16;
+                const int ln = opaque_lane(lane);
+                const int rrow = ln / 8, rch = ln % 8, lr = ln & 15, lg = ln >> 4;
+                const int64_t n = (int64_t)cur.n0 + wn * WN + rch * 8;
+                uint16_t* const dbase = static_cast<uint16_t*>(p.d);
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
-                        acc[i][j] += __builtin_bit_cast(
-                            v4f, __builtin_amdgcn_raw_buffer_load_b128(slot, sk_voff, (i * TN + j) * 1024,
-                                                                       kDeviceScope));
-            }
-            if (lost) {  // never expected: make the tile visibly wrong rather than silently short
+                        *reinterpret_cast<uint2*>(stq + lr * PITCH + (j * 16 + 4 * lg) * 2) =
+                            make_uint2(hb[i][j][0], hb[i][j][1]);
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{NAN, NAN, NAN, NAN};
+                    for (int q = 0; q < 2; ++q) {
+                        const int row = q * 8 + rrow;
+                        const uint4 v = *reinterpret_cast<const uint4*>(stq + row * PITCH + rch * 16);
+                        const int64_t m = (int64_t)cur.m0 + wm * WM + i * 16 + row;
+                        if (m < cur.m_end && n < p.N)
+                            __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v),
+                                                        reinterpret_cast<u32x4*>(dbase + m * p.ldd + n));
+                    }
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                }
             }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();  // every wave has read the partials
-            if (t == 0)
-                for (int c = sk_v + 1; c <= cur.sk_last; ++c)
-                    __hip_atomic_store(&p.sk_flag[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            store_d = false;
         }
 
         // ---- epilogue: stage each 16 x 64 block of the wave's tile in the
@@ -782,14 +903,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
             constexpr int RPI = 64 / CPR;            // rows per read / store instruction
             uint8_t* const stg = (w < 4 ? sm.a[s ^ 1] : sm.b[s ^ 1]) + (w & 3) * 8192;
             char* const dbase = static_cast<char*>(p.d) + (KIND == kGroupK ? (int64_t)cur.g * p.stride_dg * ESZ : 0);
-            const int rrow = lane / CPR, rch = lane % CPR;
+            const int ln = SK ? opaque_lane(lane) : lane;
+            const int rrow = ln / CPR, rch = ln % CPR, lr_e = ln & 15, lg_e = ln >> 4;
             const int64_t n = (int64_t)cur.n0 + wn * WN + rch * (16 / ESZ);
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const v4f v = acc[i][j];
-                    uint8_t* const dst = stg + lr * PITCH + (j * 16 + 4 * lg) * ESZ;
+                    uint8_t* const dst = stg + lr_e * PITCH + (j * 16 + 4 * lg_e) * ESZ;
                     if (OUT_F32) {
                         *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
                     } else {
@@ -843,6 +965,57 @@ __global__ __launch_bounds__(NT) void mx_gemm_kernel(GemmArgs p) {
 template <bool B1X128, bool OUT_F32>
 __global__ __launch_bounds__(NT) void gemm_sk_kernel(GemmArgs p) {
     gemm_body<kDense, B1X128 ? kScale1x128 : kScale128x128, OUT_F32, true>(p);
+}
+
+// Stream-K reduction: workgroup (t, w) adds, for wave slice w of split tile
+// t, the partial tiles of the shares v_first(t) .. v_last(t) in share order
+// and writes D (rows < M, columns < N).  A thread takes 8 of the slice's 32
+// MFMA tiles, one float4 (4 consecutive columns of one row) each.
+template <bool OUT_F32>
+__global__ __launch_bounds__(256) void sk_reduce_kernel(GemmArgs p) {
+    const int64_t t = blockIdx.x / 8;
+    const int w = blockIdx.x % 8, wm = w / WAVES_N, wn = w % WAVES_N;
+    const int lane = threadIdx.x & 63, part = threadIdx.x >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int64_t nkb = p.K / BK, I = p.sk_tiles * nkb;
+    // share holding iteration i: the largest v with v * I / sk_wgs <= i
+    const int64_t v0 = ((t * nkb + 1) * p.sk_wgs - 1) / I, v1 = (((t + 1) * nkb) * p.sk_wgs - 1) / I;
+    int64_t tm, tn;
+    grouped_order(p.sk_dp_tiles + t, p.tiles_m, p.tiles_n, tm, tn);
+#pragma unroll
+    for (int k = 0; k < TM * TN / 4; ++k) {
+        const int q = part * (TM * TN / 4) + k, i = q / TN, j = q % TN;
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int64_t v = v0; v <= v1; ++v) {
+            const float4 x = reinterpret_cast<const float4*>(p.sk_partial + (v + t) * (BM * BN))[(w * TM * TN + q) * 64 + lane];
+            if (v == v0) {
+                s = x;
+            } else {
+                s.x += x.x;
+                s.y += x.y;
+                s.z += x.z;
+                s.w += x.w;
+            }
+        }
+        const int64_t m = tm * BM + wm * WM + i * 16 + lr;
+        const int64_t n = tn * BN + wn * WN + j * 16 + 4 * lg;
+        if (m < p.M && n < p.N) {
+            if (OUT_F32) {
+                *reinterpret_cast<float4*>(static_cast<float*>(p.d) + m * p.ldd + n) = s;
+            } else {
+                const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)s.x) |
+                                    ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)s.y) << 16);
+                const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)s.z) |
+                                    ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)s.w) << 16);
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.d) + m * p.ldd + n) = make_uint2(lo, hi);
+            }
+        }
+    }
+}
+
+template <bool B1X128>
+__global__ __launch_bounds__(NT) void gemm_quant_kernel(GemmArgs p) {
+    gemm_body<kDense, B1X128 ? kScale1x128 : kScale128x128, false, 0, true>(p);
 }
 
 // Persistent grid: as many workgroups as fit on the device at once, never
@@ -923,8 +1096,6 @@ StreamK plan_kind(const GemmArgs& a, bool out_f32) {
     return out_f32 ? plan_for(gemm_sk_kernel<B1X128, true>, a) : plan_for(gemm_sk_kernel<B1X128, false>, a);
 }
 
-constexpr int64_t kSkFlagBytes = 4096;  // flag words, one per workgroup (room for 1024)
-
 }  // namespace
 
 StreamK plan_streamk(const GemmArgs& a, ScaleMode scales, bool out_f32) {
@@ -933,41 +1104,40 @@ StreamK plan_streamk(const GemmArgs& a, ScaleMode scales, bool out_f32) {
 
 int64_t streamk_workspace_bytes(const StreamK& sk) {
     if (sk.sk_tiles == 0) return 0;
-    return kSkFlagBytes + sk.sk_wgs * (int64_t)(BM * BN) * 4;
+    return (sk.sk_tiles + sk.sk_wgs) * (int64_t)(BM * BN) * 4;  // slots v + t
 }
 
 hipError_t launch_gemm_streamk(const GemmArgs& a, ScaleMode scales, bool out_f32, void* workspace,
                                int64_t workspace_bytes, hipStream_t stream) {
     const StreamK sk = plan_streamk(a, scales, out_f32);
     const int64_t need = streamk_workspace_bytes(sk);
-    if (sk.sk_tiles == 0 || sk.sk_wgs * 4 > kSkFlagBytes || workspace == nullptr || workspace_bytes < need)
+    if (sk.sk_tiles == 0 || workspace == nullptr || workspace_bytes < need)
         return launch_gemm(a, kDense, scales, out_f32, stream);
     GemmArgs g = a;
     g.sk_dp_tiles = sk.dp_tiles;
     g.sk_tiles = sk.sk_tiles;
     g.sk_wgs = sk.sk_wgs;
-    g.sk_flag = static_cast<uint32_t*>(workspace);
-    g.sk_partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + kSkFlagBytes);
-    const unsigned grid = (unsigned)sk.grid;
+    g.sk_partial = static_cast<float*>(workspace);
+    const unsigned grid = (unsigned)sk.grid, rgrid = (unsigned)(sk.sk_tiles * 8);
+    hipError_t e;
     if (scales == kScale1x128)
-        return out_f32 ? launch_grid(gemm_sk_kernel<true, true>, grid, g, stream)
-                       : launch_grid(gemm_sk_kernel<true, false>, grid, g, stream);
-    return out_f32 ? launch_grid(gemm_sk_kernel<false, true>, grid, g, stream)
-                   : launch_grid(gemm_sk_kernel<false, false>, grid, g, stream);
-}
-
-namespace {
-__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int64_t n) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
-}
-}  // namespace
-
-hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream) {
-    if (n <= 0) return hipSuccess;
-    const int64_t blocks = (n + 255) / 256;
-    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, stream, p,
-                       n);
+        e = out_f32 ? launch_grid(gemm_sk_kernel<true, true>, grid, g, stream)
+                    : launch_grid(gemm_sk_kernel<true, false>, grid, g, stream);
+    else
+        e = out_f32 ? launch_grid(gemm_sk_kernel<false, true>, grid, g, stream)
+                    : launch_grid(gemm_sk_kernel<false, false>, grid, g, stream);
+    if (e != hipSuccess) return e;
+    if (out_f32)
+        hipLaunchKernelGGL(sk_reduce_kernel<true>, dim3(rgrid), dim3(256), 0, stream, g);
+    else
+        hipLaunchKernelGGL(sk_reduce_kernel<false>, dim3(rgrid), dim3(256), 0, stream, g);
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_quant(const GemmArgs& a, ScaleMode scales, hipStream_t stream) {
+    if (a.num_tiles <= 0) return hipSuccess;
+    return scales == kScale1x128 ? launch_persistent_gemm(gemm_quant_kernel<true>, a, stream)
+                                 : launch_persistent_gemm(gemm_quant_kernel<false>, a, stream);
 }
 
 hipError_t launch_gemm(const GemmArgs& a, GroupKind kind, ScaleMode scales, bool out_f32, hipStream_t stream) {

@@ -92,11 +92,20 @@ struct GemmArgs {
     // stream-K split of a dense problem (set by launch_gemm_streamk): the
     // first sk_dp_tiles tiles are whole work items dealt round-robin over the
     // grid; the K iterations of the remaining sk_tiles tiles are divided
-    // evenly over sk_wgs workgroups; sk_flag[p] / sk_partial + p * 256 * 256
-    // hold workgroup p's partial tile for its owner (workspace)
+    // evenly over sk_wgs workgroups; sk_partial + v * 256 * 256 holds
+    // workgroup v's partial tile for its owner (workspace)
     int64_t sk_dp_tiles, sk_tiles, sk_wgs;
-    uint32_t* sk_flag;
     float* sk_partial;
+    // quantized output (bs_scaled_mm_quant): the 1x128 codes and scales of
+    // the bf16 D, rows and/or transposed columns, as bs_quant_1x128 writes them
+    uint8_t* q_row;
+    int64_t ld_qr;
+    float* s_row;
+    int64_t ld_sr;
+    uint8_t* q_col;
+    int64_t ld_qc;
+    float* s_col;
+    int64_t ld_sc;
 };
 
 // Stream-K decomposition of a dense GEMM for a given grid.
@@ -113,18 +122,17 @@ hipError_t launch_swiglu_bwd_quant(const SwigluBwdArgs& a, bool row, bool col, h
 
 hipError_t launch_gemm(const GemmArgs& a, GroupKind kind, ScaleMode scales, bool out_f32, hipStream_t stream);
 
-// Dense GEMM with the ragged last round of tiles split along K (stream-K)
-// when the workspace holds the partial tiles; otherwise as launch_gemm.
-// The workspace's flag words must be zero on entry; they are zero again when
-// the kernel ends.
+// Dense GEMM whose epilogue also writes the 1x128 quantization of its bf16
+// output (q_row / q_col of the arguments; d may be NULL).
+hipError_t launch_gemm_quant(const GemmArgs& a, ScaleMode scales, hipStream_t stream);
+
+// Dense GEMM with the ragged last round of tiles split along K (stream-K,
+// two launches) when the workspace holds the partial tiles; otherwise as
+// launch_gemm.
 StreamK plan_streamk(const GemmArgs& a, ScaleMode scales, bool out_f32);
 int64_t streamk_workspace_bytes(const StreamK& sk);
 hipError_t launch_gemm_streamk(const GemmArgs& a, ScaleMode scales, bool out_f32, void* workspace,
                                int64_t workspace_bytes, hipStream_t stream);
-
-// Zero n 32-bit words on the stream with a kernel (graph-capturable, unlike
-// a memset node).
-hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream);
 
 hipError_t launch_diag_e4m3_census(uint32_t* min_bits, uint32_t* max_bits, unsigned long long* counts,
                                    hipStream_t stream);

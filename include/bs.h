@@ -329,28 +329,61 @@ bs_status bs_scaled_mm(int64_t M, int64_t N, int64_t K,
                        hipStream_t stream);
 
 /*
+ * bs_scaled_mm_quant -- bs_scaled_mm with a bf16 output whose epilogue also
+ * quantizes that output for the next layer: the 1x128 codes and scales of
+ * the bf16 D, exactly as bs_quant_1x128 would write them from D (rows: blocks
+ * of 128 consecutive columns of a row, the next layer's forward operand;
+ * transposed columns: blocks of 128 consecutive rows of a column, its wgrad
+ * operand), from the GEMM's registers instead of a second pass over D in HBM
+ * (pages: prototype page, description -- quantization written as separate
+ * kernels is the overhead a hand-written path removes).
+ *   a, sa, b, sb, kinds, M, N, K   as bs_scaled_mm
+ *   d      optional [M, N] bf16 output (ldd >= N); NULL: D is not written
+ *   q_row, s_row   both NULL or both set: q_row[m * ld_qr + n] (ld_qr >= N),
+ *                  s_row[(n / 128) * ld_sr + m] (ld_sr >= M, multiple of 4)
+ *   q_col, s_col   both NULL or both set: q_col[n * ld_qc + m] (ld_qc >= M),
+ *                  s_col[(m / 128) * ld_sc + n] (ld_sc >= N, multiple of 4);
+ *                  requires M % 128 == 0
+ *   At least one of d, the row pair, the column pair must be set.
+ * Scale padding entries are never written.  Errors as bs_scaled_mm and
+ * bs_quant_1x128.
+ */
+bs_status bs_scaled_mm_quant(int64_t M, int64_t N, int64_t K,
+                             const uint8_t* a, int64_t lda, const float* sa, int64_t ld_sa,
+                             bs_scale_kind a_kind,
+                             const uint8_t* b, int64_t ldb, const float* sb, int64_t ld_sb,
+                             bs_scale_kind b_kind,
+                             uint16_t* d, int64_t ldd,
+                             uint8_t* q_row, int64_t ld_qr, float* s_row, int64_t ld_sr,
+                             uint8_t* q_col, int64_t ld_qc, float* s_col, int64_t ld_sc,
+                             hipStream_t stream);
+
+/*
  * bs_scaled_mm_ws -- bs_scaled_mm with a caller-provided device workspace
- * that lets the kernel balance a ragged last round of output tiles: when the
- * tiles are not a multiple of the GPU's resident workgroups, the K blocks of
- * the last round's tiles are divided evenly over all workgroups ("stream-K"),
- * and each split tile is summed by the workgroup holding its first K blocks
- * from the fp32 partial tiles the others leave in the workspace (in a fixed
- * order, so results are reproducible run to run; they may differ from
- * bs_scaled_mm's in the last bits, since the K blocks of a split tile are
- * added in a different grouping -- both are within the recipe's tolerance).
- * Same result definition as bs_scaled_mm (pages: as there; the wgrad GEMM of
- * the FFN layers leaves part of the GPU idle in its last round of tiles).
+ * that lets the GPU balance a ragged last round of output tiles: when the
+ * tiles are not a multiple of the GPU's resident workgroups and the last
+ * round is at most 3/4 full, the K blocks of the last round's tiles are
+ * divided evenly over all workgroups ("stream-K").  Two kernels on `stream`:
+ * the GEMM computes the whole tiles into D and leaves the fp32 partial tile
+ * of every piece of a split tile in the workspace; a reduction kernel adds
+ * each split tile's partials in a fixed order and writes D (results are
+ * reproducible run to run; they may differ from bs_scaled_mm's in the last
+ * bits, since a split tile's K blocks are added in a different grouping --
+ * both within the recipe's tolerance).  Same result definition as
+ * bs_scaled_mm (pages: as there; the wgrad GEMM of an FFN layer can leave
+ * part of the GPU idle in its last round of tiles).
  *
  *   All arguments as bs_scaled_mm, plus
  *   workspace        DEVICE memory, 256-byte aligned, owned by the caller;
- *                    its first 4096 bytes must be zero before the first call
- *                    that uses it (e.g. hipMemset once); every call leaves
- *                    them zero again.  NULL with workspace_bytes == 0 is
- *                    allowed.
+ *                    no initial contents are needed.  NULL with
+ *                    workspace_bytes == 0 is allowed.
  *   workspace_bytes  its size; bs_scaled_mm_workspace_bytes() gives what a
- *                    problem needs on the current device.  With less (or for
- *                    problems whose tiles fill every round) the call runs as
- *                    bs_scaled_mm and does not touch the workspace.
+ *                    problem needs on the current device (one 256 x 256
+ *                    fp32 tile per piece: split tiles + splitting
+ *                    workgroups, at most 112 MiB on MI355X).  With less (or
+ *                    for problems whose last round is full or more than 3/4
+ *                    full) the call runs as bs_scaled_mm and does not touch
+ *                    the workspace.
  * Calls that share a workspace must not overlap in time (use one stream, or
  * one workspace per stream).  Errors as bs_scaled_mm, plus BS_ERR_ALIGN for a
  * misaligned workspace and BS_ERR_NULL for a NULL one with nonzero size.
@@ -367,17 +400,16 @@ bs_status bs_scaled_mm_ws(int64_t M, int64_t N, int64_t K,
  * bs_scaled_mm_noalloc -- bs_scaled_mm_ws for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc): the same kernels, with the workspace
- * replaced by a static device array of the library, 64 MiB + 4 KiB on each
- * GPU the library runs on (held until the process ends).  The call makes no
- * allocation of any kind; the caller passes inputs and outputs only.  Each
- * call first zeroes the array's flag words with a small kernel on `stream`.
- * Every call on one GPU shares that GPU's array: calls that overlap in time
- * on one GPU (different streams, or several threads) race -- issue them on
- * one stream.  A problem whose split would need more than the array holds
- * is rejected with BS_ERR_SHAPE (not on a 256-CU GPU, which needs at most
- * 64 MiB + 4 KiB); problems that are not split run as bs_scaled_mm.
- * Arguments, result and errors as bs_scaled_mm; BS_ERR_HIP if the device
- * array cannot be located.
+ * replaced by a static device array of the library, 112 MiB on each GPU the
+ * library runs on (held until the process ends).  The call makes no
+ * allocation of any kind; the caller passes inputs and outputs only.  Every
+ * call on one GPU shares that GPU's array (no contents need to survive
+ * between calls): calls that overlap in time on one GPU (different streams,
+ * or several threads) race -- issue them on one stream.  A problem whose
+ * split would need more than the array holds is rejected with BS_ERR_SHAPE
+ * (not on a 256-CU GPU, which needs at most 112 MiB); problems that are not
+ * split run as bs_scaled_mm.  Arguments, result and errors as bs_scaled_mm;
+ * BS_ERR_HIP if the device array cannot be located.
  */
 bs_status bs_scaled_mm_noalloc(int64_t M, int64_t N, int64_t K,
                                const uint8_t* a, int64_t lda, const float* sa, int64_t ld_sa,

@@ -5,8 +5,8 @@ rounds of the GPU's resident workgroups, so the last round's tiles are split
 along K and summed through the workspace.  Checks: exact small-integer
 arithmetic bit for bit against the oracle (a missing, doubled or misplaced
 partial tile shows as an exact mismatch), random operands within the recipe's
-tolerance, the workspace's flag words back at zero after every call,
-reproducible results, and the plain kernel when the workspace is too small.
+tolerance, reproducible results, and the plain kernel when the workspace is
+too small.
 """
 
 import numpy as np
@@ -24,10 +24,6 @@ pytestmark = pytest.mark.gpu
 SHAPES = [(512, 512, 4096), (4352, 4096, 1024), (300, 640, 2048)]
 
 
-def _flags_zero(ws):
-    return bool((ws[:4096] == 0).all().item())
-
-
 @pytest.mark.parametrize("M,N,K", SHAPES)
 @pytest.mark.parametrize("kind", [bs.BS_SCALE_128X128, bs.BS_SCALE_1X128])
 def test_streamk_exact_small_integers(M, N, K, kind):
@@ -40,7 +36,7 @@ def test_streamk_exact_small_integers(M, N, K, kind):
     qb = rng.choice(SMALL_INT_CODES, size=(N, K))
     sa = np.exp2(rng.integers(-2, 3, size=(M, K // 128))).astype(np.float32)
     sb = np.exp2(rng.integers(-2, 3, size=(N // rb, K // 128))).astype(np.float32)
-    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")  # no initial contents needed
     full, out = guarded(M, N, torch.float32)
     print(f"stream-K exact M={M} N={N} K={K} kind={kind} workspace={need}", flush=True)
     bs.bs_scaled_mm_ws(torch.from_numpy(qa).cuda(), to_gpu_scales(sa), torch.from_numpy(qb).cuda(),
@@ -48,7 +44,6 @@ def test_streamk_exact_small_integers(M, N, K, kind):
     torch.cuda.synchronize()
     check_result(out, qa, sa, qb, sb, rb, exact=True)
     check_canaries(full, M, N)
-    assert _flags_zero(ws), "flag words must be zero after the call"
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -71,7 +66,6 @@ def test_streamk_tolerance_and_reproducible(M, N, K, kind):
     torch.cuda.synchronize()
     check_result(d1, qa, sa, qb, sb, rb)
     assert torch.equal(d1.view(torch.int16), d2.view(torch.int16)), "stream-K results must be reproducible"
-    assert _flags_zero(ws)
 
 
 def test_streamk_small_workspace_runs_the_plain_kernel():
