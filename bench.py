@@ -591,8 +591,9 @@ def main():
             times.append(e0.elapsed_time(e1))
         return sorted(times)[n // 2]
 
-    copy_gbs = cold_gbs = None
+    copy_gbs = cold_gbs = stream_gbs = None
     cold = {}
+    stream_ceiling = {}
     if not args.no_cold:
         # Practical HBM reference: a plain device copy of 1 GiB (torch copy_),
         # timed the same way.  The fractions above use the published 8 TB/s peak.
@@ -636,6 +637,35 @@ def main():
         cold_gbs = sum(v["work"] for v in cold.values()) / (sum(v["ms"] for v in cold.values()) * 1e-3) / 1e9
         for v in cold.values():
             v.pop("work")
+        # The practical ceiling of each quantizer pass: the streaming
+        # reference kernel (bs_diag_stream, the quantizers' access pattern)
+        # moving the same bytes -- the bf16 input read, the codes and scales
+        # written -- timed cold the same way.
+        stream_ceiling = {}
+        for name, _, work, unit in ks:
+            if unit != "GB/s":
+                continue
+            elems = work / (4.0625 if "1x128" in name else 3.0002)
+            n_read = int(2 * elems) // 16 * 16
+            n_write = int(work - 2 * elems) // 16 * 16
+            s_src = src[:n_read] if n_read <= src.numel() else torch.empty(n_read, dtype=torch.uint8, device="cuda")
+            s_dst = torch.empty(max(n_write, n_read), dtype=torch.uint8, device="cuda")
+            n_write = max(n_write, n_read)
+            times = []
+            for r in range(5):
+                torch.sum(flush_src, dim=(0,), dtype=torch.int64, out=flush_sink)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                bs.bs_diag_stream(s_src, n_read, s_dst, n_write)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            ms = sorted(times)[len(times) // 2]
+            stream_ceiling[name] = {"ms": round(ms, 4), "gbs": round((n_read + n_write) / (ms * 1e-3) / 1e9, 1),
+                                    "bytes": n_read + n_write}
+            del s_src, s_dst
+        stream_gbs = sum(v["bytes"] for v in stream_ceiling.values()) / \
+            (sum(v["ms"] for v in stream_ceiling.values()) * 1e-3) / 1e9
         del src, dst, flush_src
     del step, ks
     torch.cuda.empty_cache()
@@ -780,6 +810,9 @@ def main():
         "quant_cold_gbs": None if cold_gbs is None else round(cold_gbs, 1),
         "quant_cold_frac_of_hbm": None if cold_gbs is None else round(cold_gbs / HBM_PEAK_GBS, 4),
         "quant_cold": cold,
+        "stream_ceiling_gbs": None if stream_gbs is None else round(stream_gbs, 1),
+        "quant_cold_frac_of_stream": None if stream_gbs is None else round(cold_gbs / stream_gbs, 4),
+        "stream_ceiling": stream_ceiling,
         "kernels": per_kernel,
         "extra_configs": extra,
         "swiglu_quant_fusion": fusion,

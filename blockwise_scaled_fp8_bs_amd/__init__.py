@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     BsError,
     bs_diag_division,
     bs_diag_e4m3_census,
+    bs_diag_stream,
     bs_grouped_scaled_mm,
     bs_mx_grouped_scaled_mm,
     bs_mx_quant_1x32,

@@ -39,6 +39,7 @@ SIGNATURES = {
     "bs_last_error": (ctypes.c_char_p, []),
     "bs_diag_e4m3_census": (_E, [_P, _P, _P, _P]),
     "bs_diag_division": (_E, [_P, _P]),
+    "bs_diag_stream": (_E, [_P, _I64, _P, _I64, _P]),
 }
 
 _lib = None

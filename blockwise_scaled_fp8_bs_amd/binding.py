@@ -554,3 +554,12 @@ def bs_diag_division(device="cuda", stream=None):
     v = [int(t) for t in res.cpu().tolist()]
     return dict(zip(["pairs", "scale_mismatch", "code_mismatch", "quotient_mismatch",
                      "tiny_quotient_mismatch"], v))
+
+
+def bs_diag_stream(src, n_read, dst, n_write, stream=None):
+    """Streaming reference: read n_read bytes of ``src`` and write n_write
+    bytes of ``dst`` (uint8 GPU tensors) with the quantizers' access pattern."""
+    _require(src.is_cuda and dst.is_cuda and src.dtype == torch.uint8 and dst.dtype == torch.uint8,
+             "src and dst must be uint8 GPU tensors")
+    _require(src.numel() >= n_read and dst.numel() >= n_write, "buffers too small")
+    _check(_lib.load().bs_diag_stream(_ptr(src), n_read, _ptr(dst), n_write, _stream(stream)), "bs_diag_stream")

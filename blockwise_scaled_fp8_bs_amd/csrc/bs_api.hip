@@ -751,6 +751,17 @@ bs_status bs_diag_e4m3_census(uint32_t* min_bits, uint32_t* max_bits, unsigned l
     return hip_status(bs::launch_diag_e4m3_census(min_bits, max_bits, counts, stream), fn);
 }
 
+bs_status bs_diag_stream(const void* src, int64_t n_read, void* dst, int64_t n_write, hipStream_t stream) {
+    static const char* fn = "bs_diag_stream";
+    REQUIRE((src && dst) || n_read == 0, BS_ERR_NULL, "src and dst must be non-NULL");
+    REQUIRE(n_read >= 0 && n_write >= n_read, BS_ERR_SHAPE, "need 0 <= n_read <= n_write (got %lld, %lld)",
+            (long long)n_read, (long long)n_write);
+    REQUIRE(n_read % 16 == 0 && n_write % 16 == 0, BS_ERR_SHAPE, "n_read and n_write must be multiples of 16");
+    REQUIRE(aligned16(src) && aligned16(dst), BS_ERR_ALIGN, "src and dst must be 16-byte aligned");
+    if (n_read == 0) return ok();
+    return hip_status(bs::launch_diag_stream(src, n_read, dst, n_write, stream), fn);
+}
+
 bs_status bs_diag_division(unsigned long long* result, hipStream_t stream) {
     static const char* fn = "bs_diag_division";
     REQUIRE(result, BS_ERR_NULL, "result must be non-NULL");

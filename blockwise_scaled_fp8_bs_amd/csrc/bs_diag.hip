@@ -127,4 +127,54 @@ hipError_t launch_diag_division(unsigned long long* result, hipStream_t stream) 
     return hipGetLastError();
 }
 
+// Streaming reference for the HBM-bound kernels: reads n_read bytes of src
+// and writes n_write >= n_read bytes of dst with the quantizers' access
+// pattern (16-byte buffer loads and stores per lane, one workgroup of 256
+// threads per 32 KiB of input, coalesced), so that its rate is the practical
+// ceiling of a pass that moves the same bytes.  Written: the read bytes XOR 1
+// (nothing folds away), then the n_write - n_read remaining bytes, spread
+// evenly over the workgroups.  Both sizes are multiples of 16.
+namespace {
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const void* base, int64_t bytes) {
+    const int32_t n = bytes > 0x7fffffff ? 0x7fffffff : (bytes < 0 ? 0 : (int32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+constexpr int64_t kStreamChunk = 256 * 16 * 8;  // input bytes per workgroup
+
+__global__ __launch_bounds__(256) void stream_kernel(const uint8_t* src, int64_t n_read, uint8_t* dst,
+                                                     int64_t n_write) {
+    const int64_t base = (int64_t)blockIdx.x * kStreamChunk;
+    const int voff = threadIdx.x * 16;
+    const __amdgpu_buffer_rsrc_t rs = stream_rsrc(src + base, n_read - base);
+    const __amdgpu_buffer_rsrc_t rd = stream_rsrc(dst + base, n_read - base);
+    u32x4_t v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        v[k] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, k * 4096, 0));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) __builtin_amdgcn_raw_buffer_store_b128(v[k] ^ 1u, rd, voff, k * 4096, 0);
+    // this workgroup's part of the bytes past n_read
+    const int64_t tail = n_write - n_read;
+    const int64_t per = ((tail + gridDim.x - 1) / gridDim.x + 15) / 16 * 16;
+    const int64_t t0 = n_read + (int64_t)blockIdx.x * per;
+    if (tail > 0 && t0 < n_write) {
+        const int64_t len = (n_write - t0) < per ? (n_write - t0) : per;
+        const __amdgpu_buffer_rsrc_t rt = stream_rsrc(dst + t0, len);
+        const u32x4_t c = {(unsigned)blockIdx.x, 1u, 2u, 3u};
+        for (int64_t o = voff; o < len; o += 256 * 16) __builtin_amdgcn_raw_buffer_store_b128(c, rt, (int)o, 0, 0);
+    }
+}
+}  // namespace
+
+hipError_t launch_diag_stream(const void* src, int64_t n_read, void* dst, int64_t n_write, hipStream_t stream) {
+    const int64_t blocks = (n_read + kStreamChunk - 1) / kStreamChunk;
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(stream_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const uint8_t*>(src), n_read, static_cast<uint8_t*>(dst), n_write);
+    return hipGetLastError();
+}
+
 }  // namespace bs

@@ -137,5 +137,6 @@ hipError_t launch_gemm_streamk(const GemmArgs& a, ScaleMode scales, bool out_f32
 hipError_t launch_diag_e4m3_census(uint32_t* min_bits, uint32_t* max_bits, unsigned long long* counts,
                                    hipStream_t stream);
 hipError_t launch_diag_division(unsigned long long* result, hipStream_t stream);
+hipError_t launch_diag_stream(const void* src, int64_t n_read, void* dst, int64_t n_write, hipStream_t stream);
 
 }  // namespace bs

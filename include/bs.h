@@ -493,6 +493,18 @@ bs_status bs_diag_e4m3_census(uint32_t* min_bits, uint32_t* max_bits,
  */
 bs_status bs_diag_division(unsigned long long* result, hipStream_t stream);
 
+/*
+ * bs_diag_stream -- the streaming reference of the HBM-bound kernels: reads
+ * n_read bytes of src and writes n_write bytes of dst (n_read <= n_write,
+ * both multiples of 16, 16-byte aligned device pointers) with the
+ * quantizers' access pattern (16-byte loads and stores per lane, coalesced,
+ * one workgroup per 32 KiB of input).  Timed on the byte counts of a
+ * quantizer pass (e.g. 2 bytes read and 2.0625 written per element for 1x128
+ * rows + transposed columns) it gives the practical ceiling that pass can
+ * reach on the GPU.  The bytes written are not meaningful.
+ */
+bs_status bs_diag_stream(const void* src, int64_t n_read, void* dst, int64_t n_write, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

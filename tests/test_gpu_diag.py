@@ -57,3 +57,22 @@ def test_e4m3_encode_census_matches_oracle():
             if hi < BITS_464:
                 assert e4m3.encode(f32((hi + 1) | sgn))[0] != c
         assert covered == BITS_464 + 1
+
+
+def test_stream_reference_moves_the_bytes():
+    """The streaming reference (a timing baseline) reads every input byte and
+    writes every output byte: the first n_read written bytes are the input
+    words XOR 1, the rest are written (canary gone)."""
+    need_gpu()
+    import torch
+    n_read, n_write = 3 * 32768 + 4096, 3 * 32768 + 4096 + 3 * 1024 + 48
+    src = torch.randint(0, 256, (n_read,), dtype=torch.uint8, device="cuda")
+    dst = torch.full((n_write + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+    bs.bs_diag_stream(src, n_read, dst, n_write)
+    torch.cuda.synchronize()
+    s = src.cpu().numpy().view(np.uint32)
+    d = dst.cpu().numpy()
+    assert np.array_equal(d[:n_read].view(np.uint32), s ^ np.uint32(1))
+    tail = d[n_read:n_write].view(np.uint32).reshape(-1, 4)
+    assert np.all(tail[:, 1:] == np.array([1, 2, 3], dtype=np.uint32)), "tail bytes not written"
+    assert np.all(d[n_write:] == 0xA5), "wrote past n_write"
