@@ -241,7 +241,7 @@ def blas_threads():
     return os.cpu_count()
 
 
-def ffn_module_timing(M, D, H, median_ms, seed):
+def ffn_module_timing(M, D, H, interleaved_ms, seed):
     """Median fwd+bwd time of the fused gated FFN module and of the same FFN
     built from three Float8BlockwiseLinear layers (same weights and input)."""
     fused = bs.Float8BlockwiseGatedFFN(D, H, device="cuda")
@@ -269,7 +269,7 @@ def ffn_module_timing(M, D, H, median_ms, seed):
         clear()
         lin[2](torch.nn.functional.silu(lin[0](x)) * lin[1](x)).backward(dy)
 
-    f_ms, u_ms = median_ms(run_fused, 5), median_ms(run_unfused, 5)
+    f_ms, u_ms = interleaved_ms([run_fused, run_unfused], 7)
     flops = 2.0 * M * D * H * 3 * 3
     return {"shape": {"tokens": M, "dim": D, "hidden": H}, "fused_ms": round(f_ms, 4),
             "unfused_ms": round(u_ms, 4), "speedup": round(u_ms / f_ms, 3),
@@ -591,6 +591,23 @@ def main():
             times.append(e0.elapsed_time(e1))
         return sorted(times)[n // 2]
 
+    def interleaved_ms(fns, n=7):
+        """Median times of several variants of one piece of work, taken in
+        alternating order (a, b, ..., a, b, ...) so that the clock and heat
+        of the chip, which drift over a run, weigh on each variant alike."""
+        for fn in fns:
+            fn()
+        times = [[] for _ in fns]
+        for _ in range(n):
+            for i, fn in enumerate(fns):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times[i].append(e0.elapsed_time(e1))
+        return [sorted(t)[n // 2] for t in times]
+
     copy_gbs = cold_gbs = stream_gbs = None
     cold = {}
     stream_ceiling = {}
@@ -705,7 +722,7 @@ def main():
             def fused_qd():
                 bs.bs_scaled_mm_quant(*fargs, out=sx.out, q_row=qr_, s_row=sr_, q_col=qc_, s_col=sc_)
 
-            s_ms, q_ms, qd_ms = median_ms(sep), median_ms(fused_q), median_ms(fused_qd)
+            s_ms, q_ms, qd_ms = interleaved_ms([sep, fused_q, fused_qd])
             extra[x]["gemm_quant_epilogue"] = {
                 "separate_ms": round(s_ms, 4), "fused_ms": round(q_ms, 4), "fused_with_d_ms": round(qd_ms, 4),
                 "speedup": round(s_ms / q_ms, 3), "speedup_with_d": round(s_ms / qd_ms, 3)}
@@ -725,7 +742,7 @@ def main():
                 h = torch.nn.functional.silu(fa) * fb
                 bs.bs_quant_1x128(h, sx.qg, sx.sg, sx.qgT, sx.sgT)
 
-            f_ms, u_ms = median_ms(fused), median_ms(unfused)
+            f_ms, u_ms = interleaved_ms([fused, unfused])
             f_bytes = M_ * N_ * (2 + 2 + 1 + 1) + 4 * (M_ * N_ // 128) * 2
             fusion = {"shape": [M_, N_], "fused_ms": round(f_ms, 4), "unfused_ms": round(u_ms, 4),
                       "fused_gbs": round(f_bytes / (f_ms * 1e-3) / 1e9, 1), "speedup": round(u_ms / f_ms, 2)}
@@ -749,7 +766,7 @@ def main():
                 dab[:, N_:] = d32 * a32 * sig
                 bs.bs_quant_1x128(dab, qd, sd, qdt, sdt)
 
-            fb_ms, ub_ms = median_ms(fused_bwd), median_ms(unfused_bwd)
+            fb_ms, ub_ms = interleaved_ms([fused_bwd, unfused_bwd])
             fb_bytes = M_ * N_ * (3 * 2 + 4 * 1) + 4 * (2 * M_ * N_ // 128) * 2
             fusion_bwd = {"shape": [M_, N_], "fused_ms": round(fb_ms, 4), "unfused_ms": round(ub_ms, 4),
                           "fused_gbs": round(fb_bytes / (fb_ms * 1e-3) / 1e9, 1),
@@ -762,7 +779,7 @@ def main():
         # quantizers) against three Float8BlockwiseLinear layers with torch's
         # silu and mul: one forward + backward each.
         if not args.no_ffn_module and wx.N % 512 == 0:
-            ffn.append(ffn_module_timing(wx.M, wx.K, wx.N, median_ms, args.seed))
+            ffn.append(ffn_module_timing(wx.M, wx.K, wx.N, interleaved_ms, args.seed))
             torch.cuda.empty_cache()
 
     # MXFP8 grouped GEMMs (the pages' MoE recipe) at the pages' shapes,

@@ -137,7 +137,14 @@ __device__ __forceinline__ float bf16_from_double(double d) {
     return (float)(__bf16)f;
 }
 
-constexpr float kTieWindow = 16.0f;   // fp32 ulps; the fp32 paths err by < 6
+constexpr float kTieWindow = 16.0f;   // fp32 ulps; the fp32 paths err by < 8
+
+// tie_distance(r) > kTieWindow in two 16-bit integer instructions: the low
+// half-word of r shifted so that the window [0x8000 - 16, 0x8000 + 16] maps
+// to [0, 32].
+__device__ __forceinline__ bool off_tie(float r) {
+    return (uint16_t)(__float_as_uint(r) - (0x8000u - 16u)) > 32u;
+}
 constexpr float kMinNormal = 1.17549435e-38f;  // 2^-126
 
 // The float64 evaluations, for the few elements in a thousand the fp32 paths
@@ -160,42 +167,63 @@ __device__ __forceinline__ float2 swiglu_grad_bf16_f64(float a, float b, float d
 // float64 pass (the fp32 paths never return a true infinity: it is undecided).
 constexpr uint32_t kRedoBits = 0x7F80u;
 
+// exp(-a) in fp32 from the hardware base-2 exponential: -a log2(e) is
+// formed as a rounded head ph plus its tail pl (the product's rounding error,
+// exact by fma, and the part of log2(e) below fp32), and 2^(ph + pl) is taken
+// as 2^ph (1 + pl ln 2).  On every bf16 value a with a normal result this is
+// within 1.12 fp32 ulps of exp(-a) (the library expf: 0.76 ulps), at 6
+// instructions instead of 13; results below the normal range come out as 0,
+// where 1 + exp(-a) is 1 anyway.
+constexpr float kLog2e = 1.44269502162933349609375f;  // log2(e) rounded to fp32
+constexpr float kLog2eTail = 1.925963e-08f;           // log2(e) - kLog2e
+constexpr float kLn2 = 0.693147180559945309f;
+__device__ __forceinline__ float exp_neg(float a) {
+    const float ph = -a * kLog2e;
+    const float pl = __builtin_fmaf(-a, kLog2eTail, __builtin_fmaf(-a, kLog2e, -ph));
+    const float e = __builtin_amdgcn_exp2f(ph);
+    return __builtin_fmaf(e, pl * kLn2, e);
+}
+
 // h = silu(a) * b rounded once to bf16, in fp32; +inf (to be redone in
 // float64) where a <= -69 (exp(-a) near fp32 overflow), silu(a) is subnormal,
 // the product is not finite, or it lies near a rounding tie.  The quotient is
 // a times the hardware reciprocal of 1 + exp(-a) (1 ulp; 1 + exp(-a) >= 1 is
-// never subnormal), which adds at most 1.5 ulps to the error the tie window
-// covers.
+// never subnormal); with exp_neg's 1.12 ulps the fp32 value errs by < 8 ulps,
+// half the tie window.
 __device__ __forceinline__ float swiglu_fast(float a, float b) {
-    const float silu = a * __builtin_amdgcn_rcpf(1.0f + expf(-a));
+    const float silu = a * __builtin_amdgcn_rcpf(1.0f + exp_neg(a));
     const float r = silu * b;
     const bool normal = silu == 0.0f || fabsf(silu) >= kMinNormal;
-    const bool ok = a > -69.0f && normal && __builtin_isfinite(r) && tie_distance(r) > kTieWindow;
+    const bool ok = a > -69.0f && normal && __builtin_isfinite(r) && off_tie(r);
     return ok ? (float)(__bf16)r : __builtin_inff();
 }
 
 // da = dh * b * silu'(a) and db = dh * silu(a), silu'(a) = s (1 + a (1 - s)),
 // s = 1 / (1 + exp(-a)), in fp32, each rounded to bf16; da = +inf where
 // either rounding is not certain to be the float64 formula's (a <= -69,
-// an intermediate outside the normal range, or a value near a tie).  1 - s is
-// taken as 1 / (1 + exp(a)); near silu'(a) = 0 the sum t = 1 + a (1 - s)
-// cancels, so da's window adds 8 |a (1 - s)| / |t| ulps (infinite at t = 0),
-// written without a division.  Both reciprocals are the hardware's (1 ulp;
-// their arguments are >= 1, never subnormal): half an ulp more than a
-// correctly rounded division, inside both windows' margins.
+// an intermediate outside the normal range, or a value near a tie).  One
+// exponential serves both sigmoids: 1 - s = exp(-a) s (within 2.3 ulps of
+// 1 / (1 + exp(a)) on every bf16 a, as s is of its value).  Near
+// silu'(a) = 0 the sum t = 1 + a (1 - s) cancels, so da's window adds
+// 8 |a (1 - s)| / |t| ulps (infinite at t = 0), written without a division.
+// The reciprocal is the hardware's (1 ulp; its argument is >= 1, never
+// subnormal), inside both windows' margins.
 __device__ __forceinline__ void swiglu_grad_fast(float a, float b, float dh, float& da, float& db) {
-    const float s = __builtin_amdgcn_rcpf(1.0f + expf(-a));
-    const float sn = __builtin_amdgcn_rcpf(1.0f + expf(a));
+    const float e = exp_neg(a);
+    const float s = __builtin_amdgcn_rcpf(1.0f + e);
+    const float sn = e * s;
     const float t = __builtin_fmaf(a, sn, 1.0f);
     const float p1 = dh * b, p2 = p1 * s;
     const float rda = p2 * t;
     const float silu = a * s;
     const float rdb = dh * silu;
-    const bool ok_a = __builtin_isfinite(rda) && (p1 == 0.0f || (fabsf(p1) >= kMinNormal && fabsf(p2) >= kMinNormal)) &&
-                      (tie_distance(rda) - kTieWindow) * fabsf(t) > 8.0f * fabsf(a * sn);
-    const bool ok_b = __builtin_isfinite(rdb) && (silu == 0.0f || fabsf(silu) >= kMinNormal) &&
-                      tie_distance(rdb) > kTieWindow;
-    const bool ok = a > -69.0f && ok_a && ok_b;
+    // bitwise & of the conditions: all are cheap to evaluate, and
+    // short-circuit && would make the compiler branch per element
+    const bool ok_a = __builtin_isfinite(rda) &
+                      ((p1 == 0.0f) | ((fabsf(p1) >= kMinNormal) & (fabsf(p2) >= kMinNormal))) &
+                      ((tie_distance(rda) - kTieWindow) * fabsf(t) > 8.0f * fabsf(a * sn));
+    const bool ok_b = __builtin_isfinite(rdb) & ((silu == 0.0f) | (fabsf(silu) >= kMinNormal)) & off_tie(rdb);
+    const bool ok = (a > -69.0f) & ok_a & ok_b;
     da = ok ? (float)(__bf16)rda : __builtin_inff();
     db = (float)(__bf16)rdb;
 }
