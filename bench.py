@@ -54,10 +54,12 @@ def r4(n):
 
 # bench kernel name -> device kernel symbol (as rocprofv3 names it)
 KERNEL_SYMBOL = {
-    "quant_1x128_rowcol(A)": "quant_1x128_kernel<true, true, false>",
-    "quant_1x128_rowcol(grad_out)": "quant_1x128_kernel<true, true, false>",
+    # (prefixes: the 1x128 kernels come in a one-tile-per-workgroup and a
+    # persistent form, chosen by size)
+    "quant_1x128_rowcol(A)": "quant_1x128_kernel<true, true, false,",
+    "quant_1x128_rowcol(grad_out)": "quant_1x128_kernel<true, true, false,",
     "quant_128x128_both(W)": "quant_128x128_kernel<2>",
-    "swiglu_quant": "quant_1x128_kernel<true, true, true>",
+    "swiglu_quant": "quant_1x128_kernel<true, true, true,",
     "gemm_fwd": "gemm_kernel<0, false, false>",
     "gemm_dgrad": "gemm_kernel<0, false, false>",
     "gemm_wgrad": "gemm_kernel<0, true, false>",

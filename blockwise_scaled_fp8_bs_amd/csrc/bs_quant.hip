@@ -184,8 +184,9 @@ __device__ __forceinline__ float exp_neg(float a) {
     return __builtin_fmaf(e, pl * kLn2, e);
 }
 
-// h = silu(a) * b rounded once to bf16, in fp32; +inf (to be redone in
-// float64) where a <= -69 (exp(-a) near fp32 overflow), silu(a) is subnormal,
+// h = silu(a) * b in fp32, to be rounded once to bf16 (nearest even) by the
+// caller's packing; +inf (to be redone in float64) where a <= -69 (exp(-a)
+// near fp32 overflow), silu(a) is subnormal,
 // the product is not finite, or it lies near a rounding tie.  The quotient is
 // a times the hardware reciprocal of 1 + exp(-a) (1 ulp; 1 + exp(-a) >= 1 is
 // never subnormal); with exp_neg's 1.12 ulps the fp32 value errs by < 8 ulps,
@@ -195,11 +196,12 @@ __device__ __forceinline__ float swiglu_fast(float a, float b) {
     const float r = silu * b;
     const bool normal = silu == 0.0f || fabsf(silu) >= kMinNormal;
     const bool ok = a > -69.0f && normal && __builtin_isfinite(r) && off_tie(r);
-    return ok ? (float)(__bf16)r : __builtin_inff();
+    return ok ? r : __builtin_inff();
 }
 
 // da = dh * b * silu'(a) and db = dh * silu(a), silu'(a) = s (1 + a (1 - s)),
-// s = 1 / (1 + exp(-a)), in fp32, each rounded to bf16; da = +inf where
+// s = 1 / (1 + exp(-a)), in fp32, each to be rounded once to bf16 by the
+// caller's packing; da = +inf where
 // either rounding is not certain to be the float64 formula's (a <= -69,
 // an intermediate outside the normal range, or a value near a tie).  One
 // exponential serves both sigmoids: 1 - s = exp(-a) s (within 2.3 ulps of
@@ -224,8 +226,8 @@ __device__ __forceinline__ void swiglu_grad_fast(float a, float b, float dh, flo
                       ((tie_distance(rda) - kTieWindow) * fabsf(t) > 8.0f * fabsf(a * sn));
     const bool ok_b = __builtin_isfinite(rdb) & ((silu == 0.0f) | (fabsf(silu) >= kMinNormal)) & off_tie(rdb);
     const bool ok = (a > -69.0f) & ok_a & ok_b;
-    da = ok ? (float)(__bf16)rda : __builtin_inff();
-    db = (float)(__bf16)rdb;
+    da = ok ? rda : __builtin_inff();
+    db = rdb;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -373,11 +375,17 @@ __device__ __forceinline__ void store_raw(const Raw& raw, uint16_t* out, int64_t
 
 // 1x128 quantizer (rows and/or transposed columns).  SWIGLU quantizes
 // h = bf16(silu(x) * y) instead of x, from one read of x and y, and writes
-// h too when a.h is set.
-template <bool ROW, bool COL, bool SWIGLU>
+// h too when a.h is set.  ONE: the form for a grid of one workgroup per tile
+// (the loop then runs once): each tile's inputs are loaded where they are
+// used, with no registers held for the next tile's, so that more waves fit
+// on a SIMD.
+template <bool ROW, bool COL, bool SWIGLU, bool ONE>
 __global__ __launch_bounds__(kThreads) void quant_1x128_kernel(Quant1x128Args a) {
-    __shared__ float s_colmax[2][4][kTile];
-    __shared__ __attribute__((aligned(16))) uint8_t s_tr[COL ? 2 : 1][COL ? kTile * kTile : 16];
+    // ONE: a single LDS set (18 KiB instead of 36), a barrier between tiles
+    // in the rare case that the grid is smaller than the tile count
+    constexpr int kSets = ONE ? 1 : 2;
+    __shared__ float s_colmax[kSets][4][kTile];
+    __shared__ __attribute__((aligned(16))) uint8_t s_tr[COL ? kSets : 1][COL ? kTile * kTile : 16];
 
     const int t = threadIdx.x;
     const int tr = t >> 4, tc = t & 15;
@@ -389,13 +397,19 @@ __global__ __launch_bounds__(kThreads) void quant_1x128_kernel(Quant1x128Args a)
     const int voff_x = (8 * tr) * (int)(a.ld_x * 2) + 16 * tc;
     const int voff_y = SWIGLU ? (8 * tr) * (int)(a.ld_y * 2) + 16 * tc : 0;
     Raw raw, raw_y;
-    load_raw(a.x, a.ld_x, (tile / a.col_tiles) * kTile, (tile % a.col_tiles) * kTile, a.R, voff_x, raw);
-    if (SWIGLU)
-        load_raw(a.y, a.ld_y, (tile / a.col_tiles) * kTile, (tile % a.col_tiles) * kTile, a.R, voff_y, raw_y);
+    if (!ONE) {
+        load_raw(a.x, a.ld_x, (tile / a.col_tiles) * kTile, (tile % a.col_tiles) * kTile, a.R, voff_x, raw);
+        if (SWIGLU)
+            load_raw(a.y, a.ld_y, (tile / a.col_tiles) * kTile, (tile % a.col_tiles) * kTile, a.R, voff_y, raw_y);
+    }
 
     for (int parity = 0; tile < ntiles; tile += gridDim.x, parity ^= 1) {
         const int64_t r0 = (tile / a.col_tiles) * kTile, c0 = (tile % a.col_tiles) * kTile;
         const int64_t rows = (a.R - r0) < kTile ? (a.R - r0) : kTile;
+        if (ONE) {
+            load_raw(a.x, a.ld_x, r0, c0, a.R, voff_x, raw);
+            if (SWIGLU) load_raw(a.y, a.ld_y, r0, c0, a.R, voff_y, raw_y);
+        }
         TileRegs tl;
         Raw ph;  // gated form: h packed as bf16, +inf where the fp32 path left it undecided
         if (SWIGLU) {
@@ -415,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void quant_1x128_kernel(Quant1x128Args a)
             unpack_tile(raw, tl);
         }
         const int64_t next = tile + gridDim.x;
-        if (next < ntiles) {
+        if (!ONE && next < ntiles) {
             load_raw(a.x, a.ld_x, (next / a.col_tiles) * kTile, (next % a.col_tiles) * kTile, a.R, voff_x, raw);
             if (SWIGLU)
                 load_raw(a.y, a.ld_y, (next / a.col_tiles) * kTile, (next % a.col_tiles) * kTile, a.R, voff_y,
@@ -434,9 +448,11 @@ __global__ __launch_bounds__(kThreads) void quant_1x128_kernel(Quant1x128Args a)
             unpack_tile(ph, tl);
         }
         if (ROW) quant_tile_rows(tl, rows, a.q_row + r0 * a.ld_qr + c0, a.ld_qr, a.s_row + (c0 / kTile) * a.ld_sr + r0, tr, tc);
-        if (COL)
+        if (COL) {
             quant_tile_cols(tl, a.q_col + c0 * a.ld_qc + r0, a.ld_qc, a.s_col + (r0 / kTile) * a.ld_sc + c0,
-                            s_colmax[parity], s_tr[parity], tr, tc, wave);
+                            s_colmax[ONE ? 0 : parity], s_tr[ONE ? 0 : parity], tr, tc, wave);
+            if (ONE && tile + gridDim.x < ntiles) __syncthreads();
+        }
     }
 }
 
@@ -733,17 +749,34 @@ hipError_t launch_persistent(K kernel, const A& a, int64_t tiles, hipStream_t st
     return hipGetLastError();
 }
 
+// persistent_blocks' choice between the two forms of a kernel: `one` (no
+// prefetch) when the grid is one workgroup per tile, `persist` otherwise.
+template <typename K1, typename KP, typename A>
+hipError_t launch_one_or_persistent(K1 one, KP persist, const A& a, int64_t tiles, hipStream_t stream) {
+    const int64_t blocks = persistent_blocks(persist, tiles);
+    dim3 block(kThreads);
+    if (blocks == tiles) {
+        hipLaunchKernelGGL(one, dim3((unsigned)blocks), block, 0, stream, a);
+    } else {
+        hipLaunchKernelGGL(persist, dim3((unsigned)blocks), block, 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_quant_1x128(const Quant1x128Args& a, bool row, bool col, bool swiglu, hipStream_t stream) {
     const int64_t tiles = ((a.R + kTile - 1) / kTile) * a.col_tiles;
     if (tiles == 0) return hipSuccess;
+#define BS_Q1X128(R, C, S) \
+    launch_one_or_persistent(quant_1x128_kernel<R, C, S, true>, quant_1x128_kernel<R, C, S, false>, a, tiles, stream)
     if (swiglu) {
-        if (row && col) return launch_persistent(quant_1x128_kernel<true, true, true>, a, tiles, stream);
-        if (row) return launch_persistent(quant_1x128_kernel<true, false, true>, a, tiles, stream);
-        return launch_persistent(quant_1x128_kernel<false, true, true>, a, tiles, stream);
+        if (row && col) return BS_Q1X128(true, true, true);
+        if (row) return BS_Q1X128(true, false, true);
+        return BS_Q1X128(false, true, true);
     }
-    if (row && col) return launch_persistent(quant_1x128_kernel<true, true, false>, a, tiles, stream);
-    if (row) return launch_persistent(quant_1x128_kernel<true, false, false>, a, tiles, stream);
-    return launch_persistent(quant_1x128_kernel<false, true, false>, a, tiles, stream);
+    if (row && col) return BS_Q1X128(true, true, false);
+    if (row) return BS_Q1X128(true, false, false);
+    return BS_Q1X128(false, true, false);
+#undef BS_Q1X128
 }
 
 hipError_t launch_swiglu_bwd_quant(const SwigluBwdArgs& a, bool row, bool col, hipStream_t stream) {
