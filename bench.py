@@ -4,8 +4,8 @@ One step = every kernel of one blockwise-FP8 linear layer's training pass
 over one batch of seeded synthetic data already resident in HBM (by default
 the MoE layer: 128000 tokens over 8 experts, K 5120, N 8192):
 
-  quantize A [M, K] rows + transposed columns (1x128),
-  quantize W [N, K] (128x128) and W^T (3-D colwise layout) in one pass,
+  quantize A [M, K] rows + transposed columns (1x128) and, in the same
+    launch, W [N, K] (128x128) and W^T (3-D colwise layout) in one pass,
   quantize grad_out [M, N] rows + transposed columns (1x128),
   forward  out     = A . W^T          (1x128 x 128x128),
   dgrad    grad_in = grad_out . W     (1x128 x 128x128, via W^T),
@@ -56,9 +56,8 @@ def r4(n):
 KERNEL_SYMBOL = {
     # (prefixes: the 1x128 kernels come in a one-tile-per-workgroup and a
     # persistent form, chosen by size)
-    "quant_1x128_rowcol(A)": "quant_1x128_kernel<true, true, false,",
+    "quant_fwd_operands(A,W)": "quant_pair_kernel",
     "quant_1x128_rowcol(grad_out)": "quant_1x128_kernel<true, true, false,",
-    "quant_128x128_both(W)": "quant_128x128_kernel<2>",
     "swiglu_quant": "quant_1x128_kernel<true, true, true,",
     "gemm_fwd": "gemm_kernel<0, false, false>",
     "gemm_dgrad": "gemm_kernel<0, false, false>",
@@ -165,11 +164,15 @@ class Step:
         gemm_flops = 2.0 * M * N * K
         q1_bytes = lambda R, C: R * C * (2 + 2) + 4 * (R * C // 128) * 2  # noqa: E731
         q128b_bytes = lambda R, C: R * C * (2 + 1 + 1) + 4 * (R * C // 16384) * 2  # noqa: E731
+        # bf16 bytes each quantizer pass reads (the rest of its work is written)
+        self.quant_read_bytes = {"quant_fwd_operands(A,W)": 2 * (M * K + G * N * K),
+                                 "quant_1x128_rowcol(grad_out)": 2 * M * N}
         ks = [
-            ("quant_1x128_rowcol(A)", lambda: bs.bs_quant_1x128(self.a, self.qa, self.sa, self.qaT, self.saT),
-             q1_bytes(M, K), "GB/s"),
-            ("quant_128x128_both(W)", lambda: bs.bs_quant_128x128_both(self.w3, self.qw, self.sw, self.qwT, self.swT),
-             q128b_bytes(G * N, K), "GB/s"),
+            # the activation (1x128 rows + columns) and the weights (128x128,
+            # both layouts) in one launch
+            ("quant_fwd_operands(A,W)", lambda: bs.bs_quant_fwd_operands(
+                self.a, self.qa, self.sa, self.qaT, self.saT, self.w3, self.qw, self.sw, self.qwT, self.swT),
+             q1_bytes(M, K) + q128b_bytes(G * N, K), "GB/s"),
             ("quant_1x128_rowcol(grad_out)",
              lambda: bs.bs_quant_1x128(self.gout, self.qg, self.sg, self.qgT, self.sgT), q1_bytes(M, N), "GB/s"),
         ]
@@ -664,9 +667,8 @@ def main():
         for name, _, work, unit in ks:
             if unit != "GB/s":
                 continue
-            elems = work / (4.0625 if "1x128" in name else 3.0002)
-            n_read = int(2 * elems) // 16 * 16
-            n_write = int(work - 2 * elems) // 16 * 16
+            n_read = step.quant_read_bytes[name] // 16 * 16
+            n_write = int(work - step.quant_read_bytes[name]) // 16 * 16
             s_src = src[:n_read] if n_read <= src.numel() else torch.empty(n_read, dtype=torch.uint8, device="cuda")
             s_dst = torch.empty(max(n_write, n_read), dtype=torch.uint8, device="cuda")
             n_write = max(n_write, n_read)

@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     bs_quant_128x128_both,
     bs_quant_1x128,
     bs_quant_3d_colwise,
+    bs_quant_fwd_operands,
     bs_swiglu_bwd_quant_1x128,
     bs_swiglu_quant_1x128,
     bs_scaled_mm,

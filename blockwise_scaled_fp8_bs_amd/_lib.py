@@ -25,6 +25,9 @@ SIGNATURES = {
     "bs_quant_3d_colwise": (_E, [_P, _I64, _I64, _I64, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P]),
     "bs_quant_128x128_both": (_E, [_P, _I64, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P, _I64,
                                    _I64, _P]),
+    "bs_quant_fwd_operands": (_E, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
+                                   _P, _I64, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P, _I64,
+                                   _I64, _P]),
     "bs_scaled_mm": (_E, [_I64, _I64, _I64, _P, _I64, _P, _I64, _E, _P, _I64, _P, _I64, _E, _P, _I64, _E, _P]),
     "bs_scaled_mm_quant": (_E, [_I64, _I64, _I64, _P, _I64, _P, _I64, _E, _P, _I64, _P, _I64, _E, _P, _I64,
                                 _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P]),

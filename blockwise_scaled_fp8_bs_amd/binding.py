@@ -105,6 +105,12 @@ def bs_quant_1x128(x, q_row=None, s_row=None, q_col=None, s_col=None, stream=Non
     x [R, C] bf16; q_row [R, C] uint8 with s_row [C/128, >= R];
     q_col [C, R] uint8 with s_col [R/128, >= C].
     """
+    _check(_lib.load().bs_quant_1x128(*_quant_1x128_args(x, q_row, s_row, q_col, s_col), _stream(stream)),
+           "bs_quant_1x128")
+
+
+def _quant_1x128_args(x, q_row, s_row, q_col, s_col):
+    """Checked C arguments of bs_quant_1x128 (without the stream)."""
     _mat(x, "x", torch.bfloat16)
     R, C = x.shape
     args = [_ptr(x), R, C, _ld(x)]
@@ -122,7 +128,7 @@ def bs_quant_1x128(x, q_row=None, s_row=None, q_col=None, s_col=None, stream=Non
         args += [_ptr(q_col), _ld(q_col), _ptr(s_col), ld_sc]
     else:
         args += [None, 0, None, 0]
-    _check(_lib.load().bs_quant_1x128(*args, _stream(stream)), "bs_quant_1x128")
+    return args
 
 
 def bs_swiglu_quant_1x128(a, b, h=None, q_row=None, s_row=None, q_col=None, s_col=None, stream=None):
@@ -338,6 +344,12 @@ def bs_quant_128x128_both(x, q, s, qt, st, stream=None):
     q [G*R, C] uint8 with s [C/128, >= G*R/128]: the stacked forward layout;
     qt [G, C, R] uint8 with st [G, R/128, >= C/128]: the transposed (dgrad) layout.
     """
+    _check(_lib.load().bs_quant_128x128_both(*_quant_128x128_both_args(x, q, s, qt, st), _stream(stream)),
+           "bs_quant_128x128_both")
+
+
+def _quant_128x128_both_args(x, q, s, qt, st):
+    """Checked C arguments of bs_quant_128x128_both (without the stream)."""
     if x is not None and x.dim() == 2:
         x = x.unsqueeze(0)
     _mat(x, "x", torch.bfloat16, 3)
@@ -350,10 +362,19 @@ def bs_quant_128x128_both(x, q, s, qt, st, stream=None):
     _require(tuple(qt.shape) == (G, C, R), f"qt must be [{G}, {C}, {R}]")
     _require(st.shape[0] == G and st.shape[1] == R // 128 and st.shape[2] >= C // 128,
              f"st must be [{G}, {R // 128}, >= {C // 128}]")
-    _check(_lib.load().bs_quant_128x128_both(_ptr(x), G, R, C, x.stride(0), _ld(x), _ptr(q), _ld(q), _ptr(s), ld_s,
-                                             _ptr(qt), qt.stride(0), _ld(qt), _ptr(st), st.stride(0), st.stride(1),
-                                             _stream(stream)),
-           "bs_quant_128x128_both")
+    return [_ptr(x), G, R, C, x.stride(0), _ld(x), _ptr(q), _ld(q), _ptr(s), ld_s,
+            _ptr(qt), qt.stride(0), _ld(qt), _ptr(st), st.stride(0), st.stride(1)]
+
+
+def bs_quant_fwd_operands(x, q_row, s_row, q_col, s_col, w, qw, sw, qwt, swt, stream=None):
+    """bs_quant_1x128 of the activation x (rows and transposed columns, all
+    four outputs required) and bs_quant_128x128_both of the weights w in one
+    launch; arguments as in those two calls.  Same results, byte for byte."""
+    _require(all(t is not None for t in (q_row, s_row, q_col, s_col)),
+             "q_row, s_row, q_col and s_col are all required")
+    _check(_lib.load().bs_quant_fwd_operands(*_quant_1x128_args(x, q_row, s_row, q_col, s_col),
+                                             *_quant_128x128_both_args(w, qw, sw, qwt, swt), _stream(stream)),
+           "bs_quant_fwd_operands")
 
 
 # ----------------------------------------------------------------------------

@@ -66,11 +66,11 @@ const char* bs_last_error(void) { return g_last_error.c_str(); }
 
 namespace {
 
-// Shared by bs_quant_1x128 and bs_swiglu_quant_1x128 (y, h already checked).
-bs_status quant_1x128_common(const char* fn, const uint16_t* x, const uint16_t* y, int64_t ld_y, uint16_t* h,
-                             int64_t ld_h, int64_t R, int64_t C, int64_t ld_x, uint8_t* q_row, int64_t ld_qr,
-                             float* s_row, int64_t ld_sr, uint8_t* q_col, int64_t ld_qc, float* s_col,
-                             int64_t ld_sc, hipStream_t stream) {
+// Argument checks of the 1x128 quantizers (y, h already checked); fills *out.
+bs_status check_quant_1x128(const char* fn, const uint16_t* x, const uint16_t* y, int64_t ld_y, uint16_t* h,
+                            int64_t ld_h, int64_t R, int64_t C, int64_t ld_x, uint8_t* q_row, int64_t ld_qr,
+                            float* s_row, int64_t ld_sr, uint8_t* q_col, int64_t ld_qc, float* s_col,
+                            int64_t ld_sc, bs::Quant1x128Args* out) {
     const bool row = q_row || s_row, col = q_col || s_col;
     const bool empty = R == 0 || C == 0;
     REQUIRE(x || empty, BS_ERR_NULL, y ? "a is NULL" : "x is NULL");
@@ -110,10 +110,21 @@ bs_status quant_1x128_common(const char* fn, const uint16_t* x, const uint16_t* 
                 "q_col must be 16-byte aligned with ld_qc %% 16 == 0");
         REQUIRE(aligned16(s_col), BS_ERR_ALIGN, "s_col must be 16-byte aligned");
     }
-    if (R == 0 || C == 0) return ok();
-    bs::Quant1x128Args a{x,    R,     C,     ld_x,  q_row, ld_qr, s_row, ld_sr, q_col, ld_qc,
-                         s_col, ld_sc, C / 128, y,     ld_y,  h,     ld_h};
-    return hip_status(bs::launch_quant_1x128(a, row, col, y != nullptr, stream), fn);
+    *out = bs::Quant1x128Args{x,    R,     C,     ld_x,  q_row, ld_qr, s_row, ld_sr, q_col, ld_qc,
+                              s_col, ld_sc, C / 128, y,     ld_y,  h,     ld_h};
+    return ok();
+}
+
+// Shared by bs_quant_1x128 and bs_swiglu_quant_1x128 (y, h already checked).
+bs_status quant_1x128_common(const char* fn, const uint16_t* x, const uint16_t* y, int64_t ld_y, uint16_t* h,
+                             int64_t ld_h, int64_t R, int64_t C, int64_t ld_x, uint8_t* q_row, int64_t ld_qr,
+                             float* s_row, int64_t ld_sr, uint8_t* q_col, int64_t ld_qc, float* s_col,
+                             int64_t ld_sc, hipStream_t stream) {
+    bs::Quant1x128Args a{};
+    const bs_status st = check_quant_1x128(fn, x, y, ld_y, h, ld_h, R, C, ld_x, q_row, ld_qr, s_row, ld_sr, q_col,
+                                           ld_qc, s_col, ld_sc, &a);
+    if (st != BS_OK || R == 0 || C == 0) return st;
+    return hip_status(bs::launch_quant_1x128(a, q_row || s_row, q_col || s_col, y != nullptr, stream), fn);
 }
 
 }  // namespace
@@ -399,11 +410,13 @@ bs_status bs_quant_3d_colwise(const uint16_t* x, int64_t G, int64_t R, int64_t C
     return hip_status(bs::launch_quant_128x128(a, bs::kQ128Transposed, stream), fn);
 }
 
-bs_status bs_quant_128x128_both(const uint16_t* x, int64_t G, int64_t R, int64_t C, int64_t stride_xg,
-                                int64_t ld_x, uint8_t* q, int64_t ld_q, float* s, int64_t ld_s, uint8_t* qt,
-                                int64_t stride_qtg, int64_t ld_qt, float* st, int64_t stride_stg, int64_t ld_st,
-                                hipStream_t stream) {
-    static const char* fn = "bs_quant_128x128_both";
+namespace {
+
+// Argument checks of the two-layout 128x128 quantizer; fills *out.
+bs_status check_quant_128x128_both(const char* fn, const uint16_t* x, int64_t G, int64_t R, int64_t C,
+                                   int64_t stride_xg, int64_t ld_x, uint8_t* q, int64_t ld_q, float* s,
+                                   int64_t ld_s, uint8_t* qt, int64_t stride_qtg, int64_t ld_qt, float* st,
+                                   int64_t stride_stg, int64_t ld_st, bs::Quant128Args* out) {
     REQUIRE((x && q && s && qt && st) || G == 0 || R == 0 || C == 0, BS_ERR_NULL,
             "x, q, s, qt and st must be non-NULL");
     REQUIRE(G >= 0 && R >= 0 && C >= 0 && R % 128 == 0 && C % 128 == 0, BS_ERR_SHAPE,
@@ -434,12 +447,48 @@ bs_status bs_quant_128x128_both(const uint16_t* x, int64_t G, int64_t R, int64_t
     REQUIRE(aligned16(q) && ld_q % 16 == 0, BS_ERR_ALIGN, "q must be 16-byte aligned with ld_q %% 16 == 0");
     REQUIRE(aligned16(qt) && ld_qt % 16 == 0, BS_ERR_ALIGN, "qt must be 16-byte aligned with ld_qt %% 16 == 0");
     REQUIRE(aligned16(s) && aligned16(st), BS_ERR_ALIGN, "s and st must be 16-byte aligned");
-    if (G == 0 || R == 0 || C == 0) return ok();
     // rows of expert g are rows g*R .. of the stacked q; its scale columns
     // start at g*R/128 of each K-major row of s
-    bs::Quant128Args a{x, G, R, C, stride_xg, ld_x, q, R * ld_q, ld_q, s, R / 128, ld_s, R / 128, C / 128,
-                       qt, stride_qtg, ld_qt, st, stride_stg, ld_st};
+    *out = bs::Quant128Args{x, G, R, C, stride_xg, ld_x, q, R * ld_q, ld_q, s, R / 128, ld_s, R / 128, C / 128,
+                            qt, stride_qtg, ld_qt, st, stride_stg, ld_st};
+    return ok();
+}
+
+}  // namespace
+
+bs_status bs_quant_128x128_both(const uint16_t* x, int64_t G, int64_t R, int64_t C, int64_t stride_xg,
+                                int64_t ld_x, uint8_t* q, int64_t ld_q, float* s, int64_t ld_s, uint8_t* qt,
+                                int64_t stride_qtg, int64_t ld_qt, float* st, int64_t stride_stg, int64_t ld_st,
+                                hipStream_t stream) {
+    static const char* fn = "bs_quant_128x128_both";
+    bs::Quant128Args a{};
+    const bs_status status = check_quant_128x128_both(fn, x, G, R, C, stride_xg, ld_x, q, ld_q, s, ld_s, qt,
+                                                      stride_qtg, ld_qt, st, stride_stg, ld_st, &a);
+    if (status != BS_OK || G == 0 || R == 0 || C == 0) return status;
     return hip_status(bs::launch_quant_128x128(a, bs::kQ128Both, stream), fn);
+}
+
+bs_status bs_quant_fwd_operands(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x, uint8_t* q_row,
+                                int64_t ld_qr, float* s_row, int64_t ld_sr, uint8_t* q_col, int64_t ld_qc,
+                                float* s_col, int64_t ld_sc, const uint16_t* w, int64_t G, int64_t N, int64_t K,
+                                int64_t stride_wg, int64_t ld_w, uint8_t* qw, int64_t ld_qw, float* sw,
+                                int64_t ld_sw, uint8_t* qwt, int64_t stride_qwtg, int64_t ld_qwt, float* swt,
+                                int64_t stride_swtg, int64_t ld_swt, hipStream_t stream) {
+    static const char* fn = "bs_quant_fwd_operands";
+    const bool x_empty = R == 0 || C == 0;
+    REQUIRE((q_row && s_row && q_col && s_col) || x_empty, BS_ERR_NULL,
+            "q_row, s_row, q_col and s_col must all be set (x is quantized along rows and columns)");
+    bs::Quant1x128Args xa{};
+    bs_status status = check_quant_1x128(fn, x, nullptr, 0, nullptr, 0, R, C, ld_x, q_row, ld_qr, s_row, ld_sr,
+                                         q_col, ld_qc, s_col, ld_sc, &xa);
+    if (status != BS_OK) return status;
+    bs::Quant128Args wa{};
+    status = check_quant_128x128_both(fn, w, G, N, K, stride_wg, ld_w, qw, ld_qw, sw, ld_sw, qwt, stride_qwtg,
+                                      ld_qwt, swt, stride_swtg, ld_swt, &wa);
+    if (status != BS_OK) return status;
+    if (x_empty) xa.R = 0, xa.col_tiles = 0;
+    if (G == 0 || N == 0 || K == 0) wa.G = 0;
+    return hip_status(bs::launch_quant_pair(xa, wa, stream), fn);
 }
 
 namespace {

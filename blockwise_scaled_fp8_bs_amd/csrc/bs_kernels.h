@@ -118,6 +118,9 @@ struct StreamK {
 
 hipError_t launch_quant_1x128(const Quant1x128Args& a, bool row, bool col, bool swiglu, hipStream_t stream);
 hipError_t launch_quant_128x128(const Quant128Args& a, Quant128Mode mode, hipStream_t stream);
+// launch_quant_1x128 (rows and columns) of xa and launch_quant_128x128
+// (kQ128Both) of wa in one launch
+hipError_t launch_quant_pair(const Quant1x128Args& xa, const Quant128Args& wa, hipStream_t stream);
 hipError_t launch_swiglu_bwd_quant(const SwigluBwdArgs& a, bool row, bool col, hipStream_t stream);
 
 hipError_t launch_gemm(const GemmArgs& a, GroupKind kind, ScaleMode scales, bool out_f32, hipStream_t stream);

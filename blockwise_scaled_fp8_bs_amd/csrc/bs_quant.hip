@@ -634,9 +634,57 @@ __global__ __launch_bounds__(kThreads) void mx_quant_kernel(MxQuantArgs a) {
 // 128x128 quantizer.  MODE kQ128Rows writes the codes in place (q, s),
 // kQ128Transposed writes each tile transposed (3-D colwise: q, s), kQ128Both
 // writes both from one read of x (rows to q, s; transposed to qt, st).
+// One 128x128 tile of expert g (tile row rt, column ct) from its values tl:
+// the block amax (through wmax, 4 floats of LDS), the scale, and the codes in
+// the requested layouts (the transposed ones staged through tr_lds).
+template <int MODE>
+__device__ __forceinline__ void quant_128_tile(const Quant128Args& a, int64_t g, int64_t rt, int64_t ct,
+                                               const TileRegs& tl, float* wmax, uint8_t* tr_lds, int t, int tr,
+                                               int tc, int wave) {
+    constexpr bool ROWS = MODE != kQ128Transposed;
+    constexpr bool TRANSPOSE = MODE != kQ128Rows;
+    const int64_t r0 = rt * kTile, c0 = ct * kTile;
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(tl.f[i][j]));
+    uint32_t mb = row16_max(__float_as_uint(m));
+    mb = max(mb, (uint32_t)__shfl_xor((int)mb, 16));
+    mb = max(mb, (uint32_t)__shfl_xor((int)mb, 32));
+    if ((t & 63) == 0) wmax[wave] = __uint_as_float(mb);
+    __syncthreads();
+    const float amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const Scale sc = block_scale(amax);
+
+    if (ROWS) {
+        uint8_t* q = a.q + g * a.stride_qg;
+        const __amdgpu_buffer_rsrc_t rq = rsrc(q + r0 * a.ld_q + c0, (kTile - 1) * a.ld_q + kTile);
+        const int voff_q = (8 * tr) * (int)a.ld_q + 8 * tc;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint2 c8 = quant8(tl.f[i], sc);
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{c8.x, c8.y}, rq, voff_q, i * (int)a.ld_q, 0);
+        }
+        if (t == 0) a.s[g * a.stride_sg + ct * a.ld_s + rt] = sc.s;
+    }
+    if (TRANSPOSE) {
+        uint8_t* const qt = MODE == kQ128Both ? a.qt + g * a.stride_qtg : a.q + g * a.stride_qg;
+        float* const st = MODE == kQ128Both ? a.st + g * a.stride_stg : a.s + g * a.stride_sg;
+        const int64_t ld_qt = MODE == kQ128Both ? a.ld_qt : a.ld_q;
+        const int64_t ld_st = MODE == kQ128Both ? a.ld_st : a.ld_s;
+        Scale scs[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) scs[j] = sc;
+        uint2 codes[8];
+        col_codes(tl, scs, codes);
+        if (t == 0) st[rt * ld_st + ct] = sc.s;
+        store_transposed(tr_lds, codes, tr, tc, qt + c0 * ld_qt + r0, ld_qt);
+    }
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(Quant128Args a) {
-    constexpr bool ROWS = MODE != kQ128Transposed;
     constexpr bool TRANSPOSE = MODE != kQ128Rows;
     __shared__ float s_wmax[2][4];
     __shared__ __attribute__((aligned(16))) uint8_t s_tr[TRANSPOSE ? 2 : 1][TRANSPOSE ? kTile * kTile : 16];
@@ -664,7 +712,6 @@ __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(Quant128Args a)
 
     for (int parity = 0; tile < ntiles; tile += gridDim.x, parity ^= 1) {
         coords(tile, g, rt, ct);
-        const int64_t r0 = rt * kTile, c0 = ct * kTile;
         TileRegs tl;
         unpack_tile(raw, tl);
         const int64_t next = tile + gridDim.x;
@@ -673,45 +720,48 @@ __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(Quant128Args a)
             coords(next, ng, nrt, nct);
             load_raw(a.x + ng * a.stride_xg, a.ld_x, nrt * kTile, nct * kTile, a.R, voff_x, raw);
         }
+        quant_128_tile<MODE>(a, g, rt, ct, tl, s_wmax[parity], s_tr[TRANSPOSE ? parity : 0], t, tr, tc, wave);
+    }
+}
 
-        float m = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(tl.f[i][j]));
-        uint32_t mb = row16_max(__float_as_uint(m));
-        mb = max(mb, (uint32_t)__shfl_xor((int)mb, 16));
-        mb = max(mb, (uint32_t)__shfl_xor((int)mb, 32));
-        if ((t & 63) == 0) s_wmax[parity][wave] = __uint_as_float(mb);
-        __syncthreads();
-        const float amax = fmaxf(fmaxf(s_wmax[parity][0], s_wmax[parity][1]),
-                                 fmaxf(s_wmax[parity][2], s_wmax[parity][3]));
-        const Scale sc = block_scale(amax);
+// The forward operands of a linear layer in one launch: workgroups
+// [0, tiles_w) take the 128x128 tiles of the weights w (both layouts, as
+// quant_128x128_kernel<kQ128Both>), the rest the 128x128 tiles of x, whose
+// rows and transposed columns are quantized 1x128 (as quant_1x128_kernel).
+// One workgroup per tile (a grid-stride loop covers the rest if the grid is
+// capped), so the two passes share one ramp-up and one tail.
+__global__ __launch_bounds__(kThreads, 4) void quant_pair_kernel(Quant1x128Args xa, Quant128Args wa) {
+    __shared__ float s_colmax[4][kTile];
+    __shared__ __attribute__((aligned(16))) uint8_t s_tr[kTile * kTile];
 
-        if (ROWS) {
-            uint8_t* q = a.q + g * a.stride_qg;
-            const __amdgpu_buffer_rsrc_t rq = rsrc(q + r0 * a.ld_q + c0, (kTile - 1) * a.ld_q + kTile);
-            const int voff_q = (8 * tr) * (int)a.ld_q + 8 * tc;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint2 c8 = quant8(tl.f[i], sc);
-                __builtin_amdgcn_raw_buffer_store_b64(u32x2{c8.x, c8.y}, rq, voff_q, i * (int)a.ld_q, 0);
-            }
-            if (t == 0) a.s[g * a.stride_sg + ct * a.ld_s + rt] = sc.s;
+    const int t = threadIdx.x;
+    const int tr = t >> 4, tc = t & 15;
+    const int wave = t >> 6;
+    const int64_t per_g = wa.row_tiles * wa.col_tiles;
+    const int64_t tiles_w = wa.G * per_g;
+    const int64_t ntiles = tiles_w + ((xa.R + kTile - 1) / kTile) * xa.col_tiles;
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        Raw raw;
+        TileRegs tl;
+        if (tile < tiles_w) {
+            const int64_t g = tile / per_g, rem = tile % per_g;
+            const int64_t rt = rem / wa.col_tiles, ct = rem % wa.col_tiles;
+            load_raw(wa.x + g * wa.stride_xg, wa.ld_x, rt * kTile, ct * kTile, wa.R,
+                     (8 * tr) * (int)(wa.ld_x * 2) + 16 * tc, raw);
+            unpack_tile(raw, tl);
+            quant_128_tile<kQ128Both>(wa, g, rt, ct, tl, s_colmax[0], s_tr, t, tr, tc, wave);
+        } else {
+            const int64_t xt = tile - tiles_w;
+            const int64_t r0 = (xt / xa.col_tiles) * kTile, c0 = (xt % xa.col_tiles) * kTile;
+            const int64_t rows = (xa.R - r0) < kTile ? (xa.R - r0) : kTile;
+            load_raw(xa.x, xa.ld_x, r0, c0, xa.R, (8 * tr) * (int)(xa.ld_x * 2) + 16 * tc, raw);
+            unpack_tile(raw, tl);
+            quant_tile_rows(tl, rows, xa.q_row + r0 * xa.ld_qr + c0, xa.ld_qr,
+                            xa.s_row + (c0 / kTile) * xa.ld_sr + r0, tr, tc);
+            quant_tile_cols(tl, xa.q_col + c0 * xa.ld_qc + r0, xa.ld_qc, xa.s_col + (r0 / kTile) * xa.ld_sc + c0,
+                            s_colmax, s_tr, tr, tc, wave);
         }
-        if (TRANSPOSE) {
-            uint8_t* const qt = MODE == kQ128Both ? a.qt + g * a.stride_qtg : a.q + g * a.stride_qg;
-            float* const st = MODE == kQ128Both ? a.st + g * a.stride_stg : a.s + g * a.stride_sg;
-            const int64_t ld_qt = MODE == kQ128Both ? a.ld_qt : a.ld_q;
-            const int64_t ld_st = MODE == kQ128Both ? a.ld_st : a.ld_s;
-            Scale scs[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) scs[j] = sc;
-            uint2 codes[8];
-            col_codes(tl, scs, codes);
-            if (t == 0) st[rt * ld_st + ct] = sc.s;
-            store_transposed(s_tr[parity], codes, tr, tc, qt + c0 * ld_qt + r0, ld_qt);
-        }
+        if (tile + gridDim.x < ntiles) __syncthreads();  // LDS reused by the next tile
     }
 }
 
@@ -793,6 +843,15 @@ hipError_t launch_mx_quant(const MxQuantArgs& a, bool row, bool col, hipStream_t
     if (row && col) return launch_persistent(mx_quant_kernel<true, true>, a, tiles, stream);
     if (row) return launch_persistent(mx_quant_kernel<true, false>, a, tiles, stream);
     return launch_persistent(mx_quant_kernel<false, true>, a, tiles, stream);
+}
+
+hipError_t launch_quant_pair(const Quant1x128Args& xa, const Quant128Args& wa, hipStream_t stream) {
+    const int64_t tiles = wa.G * wa.row_tiles * wa.col_tiles + ((xa.R + kTile - 1) / kTile) * xa.col_tiles;
+    if (tiles == 0) return hipSuccess;
+    constexpr int64_t kMaxBlocks = (int64_t)1 << 23;
+    hipLaunchKernelGGL(quant_pair_kernel, dim3((unsigned)(tiles < kMaxBlocks ? tiles : kMaxBlocks)),
+                       dim3(kThreads), 0, stream, xa, wa);
+    return hipGetLastError();
 }
 
 hipError_t launch_quant_128x128(const Quant128Args& a, Quant128Mode mode, hipStream_t stream) {

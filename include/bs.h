@@ -299,6 +299,30 @@ bs_status bs_quant_128x128_both(const uint16_t* x, int64_t G, int64_t R, int64_t
                                 hipStream_t stream);
 
 /*
+ * bs_quant_fwd_operands -- the forward operands of a linear layer (or of the
+ * experts of a grouped one) quantized in one launch: bs_quant_1x128 of the
+ * activation x [R, C] along rows and transposed columns, and
+ * bs_quant_128x128_both of the weights w [G][N][K] (x's arguments first,
+ * then w's, each with exactly the meaning, layout and constraints of those
+ * two calls; all four outputs of x are required).  The results equal those
+ * of the two calls, byte for byte; one launch instead of two lets the two
+ * passes share a ramp-up and a tail (the dense passes last tens of
+ * microseconds).  Either operand may be empty.  Errors as the two calls.
+ * Pages: the prototype page, description: quantizing with separate kernels
+ * costs extra passes and launches; path forward: fast hand-written
+ * quantization.
+ */
+bs_status bs_quant_fwd_operands(const uint16_t* x, int64_t R, int64_t C, int64_t ld_x,
+                                uint8_t* q_row, int64_t ld_qr, float* s_row, int64_t ld_sr,
+                                uint8_t* q_col, int64_t ld_qc, float* s_col, int64_t ld_sc,
+                                const uint16_t* w, int64_t G, int64_t N, int64_t K,
+                                int64_t stride_wg, int64_t ld_w,
+                                uint8_t* qw, int64_t ld_qw, float* sw, int64_t ld_sw,
+                                uint8_t* qwt, int64_t stride_qwtg, int64_t ld_qwt,
+                                float* swt, int64_t stride_swtg, int64_t ld_swt,
+                                hipStream_t stream);
+
+/*
  * bs_scaled_mm -- D[M, N] = sum_kb sa(m, kb) * sb(n, kb) * P_kb[m, n],
  * P_kb = sum over k in block kb of dec(a[m][k]) * dec(b[n][k]) (fp32 MFMA),
  * accumulated in fp32 and written as bf16 (nearest-even) or fp32.

@@ -217,6 +217,40 @@ def test_quant_128x128_both_empty_is_ok(lib):
     assert _q128b(lib, G=0, x=None, q=None, s=None, qt=None, st=None) == OK
 
 
+def _qfwd(lib, x=P, R=256, C=384, ld_x=384, q_row=P, ld_qr=384, s_row=P, ld_sr=256, q_col=P, ld_qc=256,
+          s_col=P, ld_sc=384, w=P, G=2, N=256, K=384, stride_wg=256 * 384, ld_w=384, qw=P, ld_qw=384, sw=P,
+          ld_sw=4, qwt=P, stride_qwtg=384 * 256, ld_qwt=256, swt=P, stride_swtg=2 * 4, ld_swt=4):
+    return lib.bs_quant_fwd_operands(x, R, C, ld_x, q_row, ld_qr, s_row, ld_sr, q_col, ld_qc, s_col, ld_sc,
+                                     w, G, N, K, stride_wg, ld_w, qw, ld_qw, sw, ld_sw, qwt, stride_qwtg, ld_qwt,
+                                     swt, stride_swtg, ld_swt, None)
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(q_col=None), NULL, "all be set"),
+    (dict(s_row=None), NULL, "all be set"),
+    (dict(x=None), NULL, "x is NULL"),
+    (dict(C=500, ld_x=512, ld_qr=512), SHAPE, "multiple of 128"),
+    (dict(ld_sr=258), LAYOUT, "multiple of 4"),
+    (dict(x=PU), ALIGN, "aligned"),
+    (dict(qwt=None), NULL, "non-NULL"),
+    (dict(N=200), SHAPE, "multiples of 128"),
+    (dict(ld_sw=2), LAYOUT, "ld_s"),
+    (dict(stride_swtg=4), LAYOUT, "stride_stg"),
+    (dict(qw=PU), ALIGN, "q must be 16-byte aligned"),
+])
+def test_quant_fwd_operands_validation(lib, kw, code, frag):
+    """Each operand's checks are those of its own call, under this call's name."""
+    assert _qfwd(lib, **kw) == code
+    msg = lib.bs_last_error().decode()
+    assert frag in msg and "bs_quant_fwd_operands" in msg
+
+
+def test_quant_fwd_operands_empty_is_ok(lib):
+    assert _qfwd(lib, R=0, G=0, x=None, q_row=None, s_row=None, q_col=None, s_col=None, w=None, qw=None,
+                 sw=None, qwt=None, swt=None) == OK
+    assert lib.bs_last_error() == b""
+
+
 def test_leading_dimensions_are_bounded(lib):
     big = 1 << 22
     assert _q1(lib, ld_x=big) == LAYOUT and b"ld_x" in lib.bs_last_error()
