@@ -9,7 +9,7 @@ For y = x W^T with x [M, K] and W [N, K] (bf16):
 
   forward   q(x) 1x128 along K (rows), and along M (transposed, kept for wgrad)
             q(W) 128x128, and the same blocks written transposed (q(W^T) [K, N],
-            kept for dgrad), in one pass
+            kept for dgrad), in one pass -- both operands in one launch
             y        = scaled_mm(q(x), q(W))                     [M, N]
   backward  q(dy) 1x128 along N (rows) and along M (transposed)
             dx       = scaled_mm(q(dy), q(W^T))                  [M, K]
@@ -50,14 +50,19 @@ class _Float8BlockwiseLinearFn(torch.autograd.Function):
     def forward(ctx, x2, w):
         M, K = x2.shape
         N = w.shape[0]
-        qx, sx, qxt, sxt = _quant_rows_cols(x2)
-        # W in both layouts from one pass: rows for this GEMM, transposed
-        # (W^T, contiguous along N) kept for the dgrad GEMM
-        qw = torch.empty((N, K), dtype=torch.uint8, device=w.device)
-        sw = _b.empty_scales(K // 128, N // 128, w.device)
-        qwt = torch.empty((1, K, N), dtype=torch.uint8, device=w.device)
-        swt = torch.empty((1, N // 128, _b._round4(K // 128)), dtype=torch.float32, device=w.device)
-        _b.bs_quant_128x128_both(w, qw, sw, qwt, swt)
+        dev = x2.device
+        # x along rows (this GEMM) and columns (kept for the wgrad GEMM), and
+        # W in both layouts (rows for this GEMM, W^T contiguous along N kept
+        # for the dgrad GEMM), all in one launch
+        qx = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        sx = _b.empty_scales(K // 128, M, dev)
+        qxt = torch.empty((K, M), dtype=torch.uint8, device=dev)
+        sxt = _b.empty_scales(M // 128, K, dev)
+        qw = torch.empty((N, K), dtype=torch.uint8, device=dev)
+        sw = _b.empty_scales(K // 128, N // 128, dev)
+        qwt = torch.empty((1, K, N), dtype=torch.uint8, device=dev)
+        swt = torch.empty((1, N // 128, _b._round4(K // 128)), dtype=torch.float32, device=dev)
+        _b.bs_quant_fwd_operands(x2, qx, sx, qxt, sxt, w, qw, sw, qwt, swt)
         y = _b.bs_scaled_mm(qx, sx, qw, sw, _b.BS_SCALE_128X128, out_dtype=torch.bfloat16)
         ctx.save_for_backward(qxt, sxt, qwt, swt)
         ctx.w_dtype = w.dtype
