@@ -74,6 +74,7 @@ KERNEL_SYMBOL = {
 KERNEL_SOURCES = {
     "gemm_kernel": ["bs_gemm.hip", "bs_kernels.h"],
     "gemm_sk_kernel": ["bs_gemm.hip", "bs_kernels.h"],
+    "sk_reduce_kernel": ["bs_gemm.hip", "bs_kernels.h"],
     "mx_gemm_kernel": ["bs_gemm.hip", "bs_kernels.h"],
     "quant_": ["bs_quant.hip", "bs_device.h", "bs_kernels.h", "bs_mx.h"],
     "swiglu_bwd_quant_kernel": ["bs_quant.hip", "bs_device.h", "bs_kernels.h", "bs_mx.h"],
