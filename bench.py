@@ -296,6 +296,54 @@ MX_SHAPES = [
 ]
 
 
+# Dense GEMM shapes (M, N, K) at which the forward GEMM is timed next to two
+# references: the vendor's plain FP8 GEMM (hipBLASLt through
+# torch._scaled_mm, one scale per tensor, no blockwise scaling) and this
+# build's MXFP8 GEMM (same kernel body, scales applied by the MFMA, no fold).
+REFERENCE_SHAPES = [(8192, 4096, 4096), (16384, 8192, 5120), (16384, 5120, 8192), (32768, 8192, 8192)]
+
+
+def gemm_reference_timing(interleaved_ms, seed):
+    """Median times of the 128-block forward GEMM, the MX GEMM and the
+    vendor's plain FP8 GEMM on the same bf16 operands (each quantized its own
+    way), the three alternating."""
+    rows = []
+    for (M, N, K) in REFERENCE_SHAPES:
+        a = inputs.bf16_normal((M, K), 1.0, seed + 50, device="cuda")
+        w = inputs.bf16_normal((N, K), 0.02, seed + 51, device="cuda")
+        u8 = torch.uint8
+        qa, sa = torch.empty((M, K), dtype=u8, device="cuda"), bs.empty_scales(K // 128, M, "cuda")
+        qw, sw = torch.empty((N, K), dtype=u8, device="cuda"), bs.empty_scales(K // 128, N // 128, "cuda")
+        bs.bs_quant_1x128(a, qa, sa)
+        bs.bs_quant_128x128(w, qw, sw)
+        ma, msa = torch.empty((M, K), dtype=u8, device="cuda"), bs.empty_mx_scales(K // 32, M, "cuda")
+        mw, msw = torch.empty((N, K), dtype=u8, device="cuda"), bs.empty_mx_scales(K // 32, N, "cuda")
+        bs.bs_mx_quant_1x32(a, ma, msa)
+        bs.bs_mx_quant_1x32(w, mw, msw)
+        # vendor operands: one scale per tensor, amax mapped to 448
+        one = torch.ones((), device="cuda")
+        a8 = (a.float() * (448.0 / a.float().abs().max())).to(torch.float8_e4m3fn)
+        w8 = (w.float() * (448.0 / w.float().abs().max())).to(torch.float8_e4m3fn)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+        def blockwise():
+            bs.bs_scaled_mm(qa, sa, qw, sw, bs.BS_SCALE_128X128, out=out)
+
+        def mx():
+            bs.bs_mx_scaled_mm(ma, msa, mw, msw, out=out)
+
+        def vendor():
+            torch._scaled_mm(a8, w8.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+
+        t = dict(zip(("blockwise_128", "mxfp8", "vendor_plain_fp8"), interleaved_ms([blockwise, mx, vendor])))
+        flops = 2.0 * M * N * K
+        rows.append({"M": M, "N": N, "K": K, "us": {k: round(v * 1e3, 1) for k, v in t.items()},
+                     "pflops": {k: round(flops / (v * 1e-3) / 1e15, 3) for k, v in t.items()}})
+        del a, w, qa, qw, ma, mw, a8, w8, out
+        torch.cuda.empty_cache()
+    return rows
+
+
 def mx_grouped_timing(median_ms, seed, which=None):
     """Median forward and forward + backward times of mx_grouped_mm (bf16 in,
     quantization included, as the pages' op) and of torch bf16 GEMMs per
@@ -518,6 +566,8 @@ def main():
     ap.add_argument("--no-digest", action="store_true", help="skip the SHA-256 of the inputs")
     ap.add_argument("--no-ffn-module", action="store_true", help="skip the gated FFN module timing")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 grouped GEMM timings")
+    ap.add_argument("--no-references", action="store_true",
+                    help="skip the GEMM reference timings (vendor plain FP8 and MX GEMMs)")
     ap.add_argument("--mx-shapes", default=None,
                     help="comma-separated indices into the MXFP8 shape list (default: all)")
     ap.add_argument("--no-fusion", action="store_true",
@@ -794,6 +844,11 @@ def main():
         which = None if args.mx_shapes is None else {int(i) for i in args.mx_shapes.split(",")}
         mxfp8 = mx_grouped_timing(median_ms, args.seed, which)
 
+    # the forward GEMM next to the vendor's plain FP8 GEMM and the MX GEMM
+    references = None
+    if not args.no_references:
+        references = gemm_reference_timing(interleaved_ms, args.seed)
+
     cpu = None
     if not args.no_cpu_baseline:
         tflops, secs, desc = cpu_oracle_sample(w, rows=min(args.cpu_rows, w.M), seed=args.seed)
@@ -841,6 +896,7 @@ def main():
         "swiglu_bwd_quant_fusion": fusion_bwd,
         "gated_ffn_module": ffn,
         "mxfp8_grouped_mm": mxfp8,
+        "gemm_references": references,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
