@@ -398,3 +398,39 @@ def test_swiglu_bwd_every_bf16_gate_value(kind):
     q_ref, s_ref = quant.quant_1x128_rowwise(np.ascontiguousarray(np.concatenate([da, db], axis=1)[ok]))
     assert np.array_equal(u8(qr)[ok], q_ref)
     assert np.array_equal(sr.cpu().numpy().T[:R][ok], s_ref)
+
+
+def test_fused_kernels_repeat_byte_for_byte():
+    """Three runs of each fused kernel (and the plain 1x128 pass) on the same
+    8192x4096 inputs write the same bytes: the LDS exchanges of the column
+    quantization and the float64 redo loop leave nothing to timing."""
+    need_gpu()
+    M, N = 8192, 4096
+    a = inputs.bf16_normal((M, N), 1.0, 71, device="cuda")
+    b = inputs.bf16_normal((M, N), 1.0, 72, device="cuda")
+    dh = inputs.bf16_normal((M, N), 0.01, 73, device="cuda")
+
+    def outs(rows, cols):
+        return (torch.full((rows, cols), 0x5A, dtype=torch.uint8, device="cuda"),
+                bs.empty_scales(cols // 128, rows, "cuda").fill_(-7.0),
+                torch.full((cols, rows), 0x5A, dtype=torch.uint8, device="cuda"),
+                bs.empty_scales(rows // 128, cols, "cuda").fill_(-7.0))
+
+    runs = {"forward": [], "backward": [], "plain": []}
+    for _ in range(3):
+        q, s, qt, st = outs(M, N)
+        print("fused forward run", flush=True)
+        bs.bs_swiglu_quant_1x128(a, b, None, q, s, qt, st)
+        runs["forward"].append((q, s, qt, st))
+        q, s, qt, st = outs(M, 2 * N)
+        print("fused backward run", flush=True)
+        bs.bs_swiglu_bwd_quant_1x128(a, b, dh, None, q, s, qt, st)
+        runs["backward"].append((q, s, qt, st))
+        q, s, qt, st = outs(M, N)
+        bs.bs_quant_1x128(a, q, s, qt, st)
+        runs["plain"].append((q, s, qt, st))
+    torch.cuda.synchronize()
+    for what, rs in runs.items():
+        for r in rs[1:]:
+            for name, x, y in zip(("row codes", "row scales", "column codes", "column scales"), rs[0], r):
+                assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f"{what}: {name} differ between runs"
