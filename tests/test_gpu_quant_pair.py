@@ -106,3 +106,48 @@ def test_fwd_operands_equal_the_separate_calls(M, K, N):
         outs.append([t.view(torch.uint8).cpu() for t in (qr, sr, qc, sc, qw, sw, qwt, swt)])
     for name, a, b in zip(("q_row", "s_row", "q_col", "s_col", "qw", "sw", "qwt", "swt"), *outs):
         assert torch.equal(a, b), f"{name} differs between the paired launch and the separate calls"
+
+
+def test_fwd_operands_strided_views():
+    """x as a column slice of a wider tensor (ld_x > C) and the weights as
+    experts of a padded stack (stride between experts > N * ld_w, ld_w > K):
+    same bytes as the oracle on the logical values."""
+    need_gpu()
+    R, C, G, N, K = 384, 256, 2, 256, 384
+    xs = torch.zeros((R, C + 64), dtype=torch.bfloat16)
+    xs[:, 32:32 + C] = special_input(R, C, seed=5)
+    ws = torch.zeros((G, N + 128, K + 32), dtype=torch.bfloat16)
+    for g in range(G):
+        ws[g, :N, 16:16 + K] = special_input(N, K, seed=9 + g, sigma=0.02)
+    xg = xs.cuda()[:, 32:32 + C]
+    wg = ws.cuda()[:, :N, 16:16 + K]
+    assert xg.stride(0) == C + 64 and wg.stride(1) == K + 32 and wg.stride(0) == (N + 128) * (K + 32)
+    qr_full, qr = guarded(R, C, torch.uint8)
+    sr_full, sr = scale_buffer(C // 128, R)
+    qc_full, qc = guarded(C, R, torch.uint8)
+    sc_full, sc = scale_buffer(R // 128, C)
+    (q_full, s_full, qt_full, st_full), (qw, sw, qwt, swt) = _weight_buffers(G, N, K)
+    print("quant_fwd_operands strided views", flush=True)
+    bs.bs_quant_fwd_operands(xg, qr, sr, qc, sc, wg, qw, sw, qwt, swt)
+    torch.cuda.synchronize()
+    xb = bits16(xs[:, 32:32 + C].contiguous())
+    q_ref, s_ref = quant.quant_1x128_rowwise(xb)
+    assert_codes(qr, q_ref)
+    assert_scales(sr, s_ref)
+    q_ref, s_ref = quant.quant_1x128_colwise(xb)
+    assert_codes(qc, q_ref)
+    assert_scales(sc, s_ref)
+    check_canaries(qr_full, R, C)
+    check_canaries(qc_full, C, R)
+    check_scale_canaries(sr_full, C // 128, R)
+    check_scale_canaries(sc_full, R // 128, C)
+    wb = bits16(ws[:, :N, 16:16 + K].contiguous())
+    q_ref, s_ref = quant.quant_128x128(wb.reshape(G * N, K))
+    qt_ref, st_ref = quant.quant_3d_colwise(wb)
+    assert np.array_equal(u8(q_full)[:G * N, :K], q_ref)
+    sa = s_full.cpu().view(torch.int32).numpy().view(np.uint32)
+    assert np.array_equal(sa[:K // 128, :G * N // 128], np.ascontiguousarray(s_ref.T).view(np.uint32))
+    assert np.array_equal(u8(qt_full)[:G, :, :N], qt_ref)
+    sta = st_full.cpu().view(torch.int32).numpy().view(np.uint32)
+    for g in range(G):
+        assert np.array_equal(sta[g, :, :K // 128], np.ascontiguousarray(st_ref[g].T).view(np.uint32))
