@@ -4,6 +4,7 @@
 #include <cstdio>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/bs.h"
 #include "bs_kernels.h"
@@ -46,6 +47,45 @@ bs_status hip_status(hipError_t e, const char* fn) {
     } while (0)
 
 }  // namespace
+
+namespace bs {
+
+DeviceFit device_fit(const void* kernel, int threads, int default_per_cu) {
+    struct Entry {
+        int dev;
+        const void* kernel;
+        int threads;
+        DeviceFit fit;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> cache;
+    int dev = -1;
+    const bool have_dev = hipGetDevice(&dev) == hipSuccess;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (const Entry& e : cache)
+            if (have_dev && e.dev == dev && e.kernel == kernel && e.threads == threads) return e.fit;
+    }
+    DeviceFit fit{256, default_per_cu};
+    bool complete = have_dev;
+    int v = 0;
+    if (have_dev && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+        fit.cus = v;
+    else
+        complete = false;
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, 0) == hipSuccess && occ > 0)
+        fit.per_cu = occ;
+    else
+        complete = false;
+    if (complete) {  // only answers from the runtime are kept
+        std::lock_guard<std::mutex> lock(mu);
+        cache.push_back(Entry{dev, kernel, threads, fit});
+    }
+    return fit;
+}
+
+}  // namespace bs
 
 extern "C" {
 

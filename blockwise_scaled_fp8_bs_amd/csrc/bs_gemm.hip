@@ -1022,14 +1022,8 @@ __global__ __launch_bounds__(NT) void gemm_quant_kernel(GemmArgs p) {
 // more than the tiles.
 template <typename Kern>
 unsigned persistent_grid(Kern kernel, int64_t tiles) {
-    int dev = 0, cus = 256, per_cu = 1;
-    if (hipGetDevice(&dev) == hipSuccess) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
-    }
-    int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, NT, 0) == hipSuccess && occ > 0) per_cu = occ;
-    const int64_t cap = (int64_t)cus * per_cu;
+    const DeviceFit fit = device_fit(reinterpret_cast<const void*>(kernel), NT, 1);
+    const int64_t cap = (int64_t)fit.cus * fit.per_cu;
     return (unsigned)(tiles < cap ? tiles : cap);
 }
 

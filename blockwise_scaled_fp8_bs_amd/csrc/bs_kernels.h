@@ -137,6 +137,17 @@ int64_t streamk_workspace_bytes(const StreamK& sk);
 hipError_t launch_gemm_streamk(const GemmArgs& a, ScaleMode scales, bool out_f32, void* workspace,
                                int64_t workspace_bytes, hipStream_t stream);
 
+// CUs of the current device and resident workgroups of `kernel` (`threads`
+// per workgroup) per CU, for sizing persistent grids.  Queried once per
+// (device, kernel, threads) and kept: the two runtime queries cost several
+// microseconds per launch and their answers never change.  A failed query
+// falls back to 256 CUs and `default_per_cu`.
+struct DeviceFit {
+    int cus;
+    int per_cu;
+};
+DeviceFit device_fit(const void* kernel, int threads, int default_per_cu);
+
 hipError_t launch_diag_e4m3_census(uint32_t* min_bits, uint32_t* max_bits, unsigned long long* counts,
                                    hipStream_t stream);
 hipError_t launch_diag_division(unsigned long long* result, hipStream_t stream);

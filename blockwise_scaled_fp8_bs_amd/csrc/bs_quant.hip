@@ -778,14 +778,8 @@ __global__ __launch_bounds__(kThreads, 4) void quant_pair_kernel(Quant1x128Args 
 // persistent.
 template <typename K>
 int64_t persistent_blocks(K kernel, int64_t tiles) {
-    int dev = 0, cus = 256, per_cu = 2;
-    if (hipGetDevice(&dev) == hipSuccess) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
-    }
-    int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, 0) == hipSuccess && occ > 0) per_cu = occ;
-    const int64_t cap = (int64_t)cus * per_cu;
+    const DeviceFit fit = device_fit(reinterpret_cast<const void*>(kernel), kThreads, 2);
+    const int64_t cap = (int64_t)fit.cus * fit.per_cu;
     // (capped at 2^23 workgroups, 2^31 threads; the grid-stride loop takes the rest)
     constexpr int64_t kMaxBlocks = (int64_t)1 << 23;
     if (tiles >= 2 * cap) return tiles < kMaxBlocks ? tiles : kMaxBlocks;
