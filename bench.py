@@ -79,6 +79,7 @@ KERNEL_SOURCES = {
     "quant_": ["bs_quant.hip", "bs_device.h", "bs_kernels.h", "bs_mx.h"],
     "swiglu_bwd_quant_kernel": ["bs_quant.hip", "bs_device.h", "bs_kernels.h", "bs_mx.h"],
     "mx_quant_kernel": ["bs_quant.hip", "bs_device.h", "bs_kernels.h", "bs_mx.h"],
+    "stream_kernel": ["bs_diag.hip", "bs_kernels.h"],
 }
 
 
