@@ -56,7 +56,14 @@ constexpr int NT = 512;
 constexpr int WAVES_N = 4;
 constexpr int WM = 128, WN = 64;
 constexpr int TM = WM / 16, TN = WN / 16;
-constexpr int kGroupRows = 8;  // tile rows per L2 group
+constexpr int kGroupRows = 8;   // tile rows per L2 group
+// GROUP_M: 4 tile rows per L2 group.  An XCD's rows of a small expert can be
+// a slice of 0-3 tile rows, so an 8-row group often spans three experts and
+// its 32 concurrent tiles need the B panels of all three.  With 4 rows, over
+// the random group sizes of the 128000-token MoE layer: forward 15.1 instead
+// of 18.5 GB fetched and 1-3 % faster, dgrad 7 % faster; with equal groups
+// both unchanged within 1 %.
+constexpr int kGroupRowsM = 4;
 constexpr int kChunks = BK / 32;  // MX blocks per K block
 constexpr int kMxPitch = BM + 16;  // MX scale bytes staged per chunk: 256 rows from a 16-byte aligned start
 
@@ -104,11 +111,12 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t n) {
     return x * q + (x < r ? x : r) + j;
 }
 
+template <int ROWS = kGroupRows>
 __device__ __forceinline__ void grouped_order(int64_t L, int64_t tiles_m, int64_t tiles_n, int64_t& tm,
                                               int64_t& tn) {
-    const int64_t per_group = kGroupRows * tiles_n;
-    const int64_t first = (L / per_group) * kGroupRows;
-    const int64_t gm = (tiles_m - first) < kGroupRows ? (tiles_m - first) : kGroupRows;
+    const int64_t per_group = ROWS * tiles_n;
+    const int64_t first = (L / per_group) * ROWS;
+    const int64_t gm = (tiles_m - first) < ROWS ? (tiles_m - first) : ROWS;
     const int64_t r = L % per_group;
     tm = first + r % gm;
     tn = r / gm;
@@ -230,7 +238,7 @@ __device__ __forceinline__ void resolve_tile(const GemmArgs& p, int64_t idx, int
         // (and the buffer descriptors built from it) in scalar registers.
         auto lds = [](const int32_t* a, int i) { return __builtin_amdgcn_readfirstlane(a[i]); };
         int64_t tr, tn;
-        grouped_order(L, rows, p.tiles_n, tr, tn);
+        grouped_order<kGroupRowsM>(L, rows, p.tiles_n, tr, tn);
         int lo = 0, hi = 8 * (int)p.G - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -245,7 +253,7 @@ __device__ __forceinline__ void resolve_tile(const GemmArgs& p, int64_t idx, int
         t.g = g;
     } else if (KIND == kGroupM) {
         int64_t tr, tn;
-        grouped_order(L, rows, p.tiles_n, tr, tn);
+        grouped_order<kGroupRowsM>(L, rows, p.tiles_n, tr, tn);
         int64_t before = 0, prev = 0;
         t.m0 = (int32_t)p.M;
         t.m_end = (int32_t)p.M;
