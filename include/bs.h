@@ -42,9 +42,11 @@
  *     contiguous, s[kb * ld_s + row] or s[kb * ld_s + row / 128], and ld_s is
  *     a multiple of 4 (16 bytes).  One layout serves every scale tensor.
  *     Scale padding entries (index >= the logical count) are never written.
- *   - Ownership: the caller owns every buffer.  The library allocates nothing,
- *     keeps no state between calls and is thread-safe.  Outputs must not
- *     alias inputs or each other.
+ *   - Ownership: the caller owns every buffer.  The library allocates nothing
+ *     and is thread-safe; between calls it keeps only a host-side cache of
+ *     device properties (CU count, resident workgroups per kernel) and the
+ *     static device array of bs_scaled_mm_noalloc.  Outputs must not alias
+ *     inputs or each other.
  *   - Execution: every call validates its arguments on the host, then
  *     enqueues its kernels on `stream` (NULL = the default stream) and returns
  *     without synchronizing.  Nothing is enqueued when validation fails.
