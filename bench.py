@@ -24,13 +24,15 @@ bounded sample of the same workload on the host (rank 0, N = 1).
 
 The line also carries: the SHA-256 of the bf16 inputs (the bytes both the
 GPU and the oracle consume), the shader and memory clocks sampled while the
-timed steps ran, and a short record of each dense workload (forward, dgrad
-and wgrad of one linear layer) timed the same way.
+timed steps ran, a short record of each dense workload (forward, dgrad
+and wgrad of one linear layer) timed the same way, and the smallest layer's
+forward (256x512x256, launch-bound) as eager calls and as one HIP graph.
 """
 
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -304,6 +306,63 @@ MX_SHAPES = [
 REFERENCE_SHAPES = [(8192, 4096, 4096), (16384, 8192, 5120), (16384, 5120, 8192), (32768, 8192, 8192)]
 
 
+def launch_bound_timing(seed, n=300):
+    """The smallest workload, the 256x512x256 linear forward (x quantized 1x128,
+    W 128x128, the forward GEMM: three calls of a few microseconds each), is
+    bound by launch overhead: time it as eager calls and as one replayed HIP
+    graph of the same calls (the library enqueues only kernels and never
+    synchronizes, so the calls capture as they are), and check that a replay
+    writes the eager output bit for bit."""
+    w = inputs.WORKLOADS["linear_fwd_256x512x256"]
+    M, K, N = w.M, w.K, w.N
+    x = inputs.bf16_normal((M, K), w.sigma_a, seed, device="cuda")
+    wt = inputs.bf16_normal((N, K), w.sigma_w, seed + 1, device="cuda")
+    qx = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sx = bs.empty_scales(K // 128, M, "cuda")
+    qw = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sw = bs.empty_scales(K // 128, N // 128, "cuda")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def fwd():
+        bs.bs_quant_1x128(x, q_row=qx, s_row=sx)
+        bs.bs_quant_128x128(wt, qw, sw)
+        bs.bs_scaled_mm(qx, sx, qw, sw, bs.BS_SCALE_128X128, out=out)
+
+    for _ in range(10):
+        fwd()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph):
+            fwd()
+    torch.cuda.current_stream().wait_stream(side)
+    out.fill_(float("nan"))
+    graph.replay()
+    torch.cuda.synchronize()
+    equal = bool(torch.equal(out.view(torch.int16), ref.view(torch.int16)))
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n * 1e6
+
+    eager_us, graph_us = [], []
+    for _ in range(3):
+        eager_us.append(timed(fwd))
+        graph_us.append(timed(graph.replay))
+    e, g = statistics.median(eager_us), statistics.median(graph_us)
+    del graph
+    return {"workload": w.name, "calls": 3, "eager_us_per_step": round(e, 1), "graph_us_per_step": round(g, 1),
+            "speedup": round(e / g, 2), "graph_output_equal": equal}
+
+
 def gemm_reference_timing(interleaved_ms, seed):
     """Median times of the 128-block forward GEMM, the MX GEMM and the
     vendor's plain FP8 GEMM on the same bf16 operands (each quantized its own
@@ -574,6 +633,7 @@ def main():
     ap.add_argument("--no-fusion", action="store_true",
                     help="skip the fused gated-activation timings (keeps per-kernel profiles to the step's shapes)")
     ap.add_argument("--no-cold", action="store_true", help="skip the copy reference and the cold-cache quantizers")
+    ap.add_argument("--no-graph", action="store_true", help="skip the eager vs HIP-graph timing of the smallest layer")
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="tokens of the workload the CPU oracle baseline runs on (capped at M)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -850,6 +910,10 @@ def main():
     if not args.no_references:
         references = gemm_reference_timing(interleaved_ms, args.seed)
 
+    graph = None
+    if not args.no_graph:
+        graph = launch_bound_timing(args.seed)
+
     cpu = None
     if not args.no_cpu_baseline:
         tflops, secs, desc = cpu_oracle_sample(w, rows=min(args.cpu_rows, w.M), seed=args.seed)
@@ -898,6 +962,7 @@ def main():
         "gated_ffn_module": ffn,
         "mxfp8_grouped_mm": mxfp8,
         "gemm_references": references,
+        "launch_bound_graph": graph,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
