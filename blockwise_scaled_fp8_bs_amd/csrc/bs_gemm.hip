@@ -652,13 +652,19 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
                 dma4(o.sb, lds_addr(&sm.sb[s].f[0]), voff_s, (int)((int64_t)kb * p.ld_sb * 4));
         }
     };
-    auto issue_loads = [&](const Operands& o, int32_t kb, int s) {
+    // Copy c = 0..7 of this wave's share: A for even c, B for odd c, rows
+    // [(8i + w) * 8, +8) of round i = c / 2.
+    auto issue_copy = [&](const Operands& o, int32_t kb, int s, int c) {
         const int k_off = kb * BK;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        const int i = c >> 1;
+        if ((c & 1) == 0)
             dma16(o.a, lds_addr(&sm.a[s][(8 * i + w) * 1024]), voff_a, k_off + (int)(64 * i * p.lda));
+        else
             dma16(o.b, lds_addr(&sm.b[s][(8 * i + w) * 1024]), voff_b, k_off + (int)(64 * i * p.ldb));
-        }
+    };
+    auto issue_loads = [&](const Operands& o, int32_t kb, int s) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) issue_copy(o, kb, s, c);
         issue_scales(o, kb, s, 0);
     };
     // The same copies issued by the four waves of group g alone (rows
@@ -679,25 +685,18 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
         }
         issue_scales(o, kb, s, 4 * g);
     };
-    // Piece k of issue_loads_group's copies for wave group g: k < 16 one
-    // operand copy (A for even k, B for odd k, round k / 2), k == 16 the scales.
-    auto issue_piece = [&](const Operands& o, int32_t kb, int s, int g, int k) {
-        const int k_off = kb * BK;
-        const int i = k >> 1;
-        if (k == 16)
-            issue_scales(o, kb, s, 4 * g);
-        else if ((k & 1) == 0)
-            dma16(o.a, lds_addr(&sm.a[s][(4 * i + wq) * 1024]), voff_a4, k_off + (int)(32 * i * p.lda));
-        else
-            dma16(o.b, lds_addr(&sm.b[s][(4 * i + wq) * 1024]), voff_b4, k_off + (int)(32 * i * p.ldb));
-    };
-    // With 128x128 B scales (forward and dgrad) the issuing group spreads
-    // its copies over its first 9 MFMAs, two per MFMA, instead of issuing
-    // all 17 before them: its waves then join the matrix pipes early, and
-    // every copy is still issued in the first quarter of the K block (3-4 %
-    // faster on the dense and FFN shapes).  The 1x128 x 1x128 kernel needs
-    // its registers for the per-element fold and keeps the block issue; so
-    // does the MX kernel (no gain measured).
+    // With 128x128 B scales (forward and dgrad) all eight waves share the
+    // next K block's copies instead: wave w issues its issue_copy pieces, one
+    // after each of its first 8 MFMAs (waves 0 and 1 the scales with the
+    // first), so every copy is still issued in the first quarter of the
+    // block.  Both waves of a SIMD then carry the same load and reach the
+    // block-end barrier together: with one group issuing, the other group
+    // spent 16-24 % of its time waiting there, and the shared issue is 3-5 %
+    // faster on the forward (the one-group spread was itself 3-4 % faster
+    // than issuing every copy before the first MFMA).  The 1x128 x 1x128
+    // kernel keeps the block issue by one group (its per-element fold leaves
+    // no registers: spreading its copies spills, and measured no gain); so
+    // does the MX kernel (shared spread issue 4 % slower).
     constexpr bool kSpread = !MX && !B1X128 && KIND != kGroupK;
     // An MFMA operand fragment: logical chunks 2 lg and 2 lg + 1 of the row
     // (for MX, K chunks lg and lg + 4: see the copies above).
@@ -752,7 +751,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
             for (int j = 0; j < TN; ++j) acc[i][j] = zero;
 
         for (int32_t it = 0; it < nkb; ++it) {
-            const bool spread = kSpread && it + 1 < nkb && (w >> 2) == (it & 1);
+            const bool spread = kSpread && it + 1 < nkb;
             if (it + 1 < nkb) {
                 if (!kSpread) issue_loads_group(ops, cur.kb0 + it + 1, s ^ 1, it & 1);
             } else if (has_next) {
@@ -824,9 +823,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
                         const int q = i * TN + j;
                         pbuf[q & 1] =
                             __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, zero, 0, 0, 0, 0, 0, 0);
-                        if (kSpread && q <= 8 && spread) {
-                            issue_piece(ops, cur.kb0 + it + 1, s ^ 1, it & 1, 2 * q);
-                            if (q < 8) issue_piece(ops, cur.kb0 + it + 1, s ^ 1, it & 1, 2 * q + 1);
+                        if (kSpread && q < 8 && spread) {
+                            if (q == 0) issue_scales(ops, cur.kb0 + it + 1, s ^ 1, 0);
+                            issue_copy(ops, cur.kb0 + it + 1, s ^ 1, q);
                         }
                         if (q > 0) fold(pbuf[(q - 1) & 1], pi, pj);
                         pi = i;
