@@ -56,14 +56,18 @@ constexpr int NT = 512;
 constexpr int WAVES_N = 4;
 constexpr int WM = 128, WN = 64;
 constexpr int TM = WM / 16, TN = WN / 16;
-constexpr int kGroupRows = 8;   // tile rows per L2 group
-// GROUP_M: 4 tile rows per L2 group.  An XCD's rows of a small expert can be
-// a slice of 0-3 tile rows, so an 8-row group often spans three experts and
-// its 32 concurrent tiles need the B panels of all three.  With 4 rows, over
-// the random group sizes of the 128000-token MoE layer: forward 15.1 instead
-// of 18.5 GB fetched and 1-3 % faster, dgrad 7 % faster; with equal groups
-// both unchanged within 1 %.
-constexpr int kGroupRowsM = 4;
+// Tile rows per L2 group (tiles are walked down the group's rows first).
+// Dense and GROUP_M: 4.  An XCD's rows of a small expert can be a slice of
+// 0-3 tile rows, so an 8-row group often spans three experts and its 32
+// concurrent tiles need the B panels of all three; with 4 rows, over the
+// random group sizes of the 128000-token MoE layer, the forward fetched 15.1
+// instead of 18.5 GB and ran 1-3 % faster, the dgrad 7 % faster (equal
+// groups: both unchanged within 1 %).  On the dense layers 4 rows are 2-7 %
+// faster than 8 for the forward and dgrad (16384x5120x8192 forward 7 %,
+// 16384x7168x2048 forward 1 % slower), 2 rows mixed, 16 no better.
+// GROUP_K and stream-K: 8 (GROUP_K with 4: same time, with 2: 3 % slower).
+constexpr int kGroupRows = 4;
+constexpr int kGroupRowsK = 8;
 constexpr int kChunks = BK / 32;  // MX blocks per K block
 constexpr int kMxPitch = BM + 16;  // MX scale bytes staged per chunk: 256 rows from a 16-byte aligned start
 
@@ -194,7 +198,7 @@ __device__ __forceinline__ void sk_work(const GemmArgs& p, const SkPlan& s, int6
         t.sk_last = s.v + tt;  // the piece's slot
     }
     int64_t tm, tn;
-    grouped_order(L, p.tiles_m, p.tiles_n, tm, tn);
+    grouped_order<kGroupRowsK>(L, p.tiles_m, p.tiles_n, tm, tn);
     t.m0 = uni(tm * BM);
     t.n0 = uni(tn * BN);
 }
@@ -238,7 +242,7 @@ __device__ __forceinline__ void resolve_tile(const GemmArgs& p, int64_t idx, int
         // (and the buffer descriptors built from it) in scalar registers.
         auto lds = [](const int32_t* a, int i) { return __builtin_amdgcn_readfirstlane(a[i]); };
         int64_t tr, tn;
-        grouped_order<kGroupRowsM>(L, rows, p.tiles_n, tr, tn);
+        grouped_order(L, rows, p.tiles_n, tr, tn);
         int lo = 0, hi = 8 * (int)p.G - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -253,7 +257,7 @@ __device__ __forceinline__ void resolve_tile(const GemmArgs& p, int64_t idx, int
         t.g = g;
     } else if (KIND == kGroupM) {
         int64_t tr, tn;
-        grouped_order<kGroupRowsM>(L, rows, p.tiles_n, tr, tn);
+        grouped_order(L, rows, p.tiles_n, tr, tn);
         int64_t before = 0, prev = 0;
         t.m0 = (int32_t)p.M;
         t.m_end = (int32_t)p.M;
@@ -289,7 +293,7 @@ __device__ __forceinline__ void resolve_tile(const GemmArgs& p, int64_t idx, int
         const int64_t rank = Lk / per_g;
         const int64_t g = p.G <= kMaxRankedGroups ? group_by_rank[rank] : rank;
         int64_t tm, tn;
-        grouped_order(Lk % per_g, p.tiles_m, p.tiles_n, tm, tn);
+        grouped_order<kGroupRowsK>(Lk % per_g, p.tiles_m, p.tiles_n, tm, tn);
         int64_t s = 0, e = 0;
         for (int64_t h = 0; h <= g; ++h) {
             s = e;
@@ -988,7 +992,7 @@ __global__ __launch_bounds__(256) void sk_reduce_kernel(GemmArgs p) {
     // share holding iteration i: the largest v with v * I / sk_wgs <= i
     const int64_t v0 = ((t * nkb + 1) * p.sk_wgs - 1) / I, v1 = (((t + 1) * nkb) * p.sk_wgs - 1) / I;
     int64_t tm, tn;
-    grouped_order(p.sk_dp_tiles + t, p.tiles_m, p.tiles_n, tm, tn);
+    grouped_order<kGroupRowsK>(p.sk_dp_tiles + t, p.tiles_m, p.tiles_n, tm, tn);
 #pragma unroll
     for (int k = 0; k < TM * TN / 4; ++k) {
         const int q = part * (TM * TN / 4) + k, i = q / TN, j = q % TN;
