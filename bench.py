@@ -85,8 +85,35 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text):
+    """C++ source with its comments removed and whitespace runs collapsed
+    (string and character literals kept as written)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash(symbol):
-    """sha256 prefix of the sources of the device kernel `symbol`."""
+    """sha256 prefix of the code of the sources of the device kernel
+    `symbol`, comments and whitespace left out (editing a comment does not
+    make counters taken on the same code stale)."""
     import hashlib
     src = os.path.join(ROOT, "blockwise_scaled_fp8_bs_amd", "csrc")
     files = next((fs for prefix, fs in KERNEL_SOURCES.items() if symbol.startswith(prefix)), None)
@@ -94,7 +121,8 @@ def kernel_source_hash(symbol):
         return None
     h = hashlib.sha256()
     for f in files:
-        h.update(open(os.path.join(src, f), "rb").read())
+        h.update(_code_only(open(os.path.join(src, f), encoding="utf-8").read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

@@ -675,7 +675,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
     // [(4i + w % 4) * 8, +8) in round i = 0..7).  Copies stall the issuing
     // wave while the CU's address unit works through them (about 1 KiB per
     // 16 cycles); with one group issuing per K block, the other group's
-    // waves go straight to their MFMAs and keep the matrix pipes busy.
+    // waves go straight to their MFMAs and keep the matrix pipes busy.  The
+    // 1x128 x 1x128 and MX kernels issue this way, at the start of each
+    // block: every wave issuing its share there was 1.5-3 % slower, and so
+    // was splitting the wgrad's copies (A by the group at the block start,
+    // B by every wave after one of its first MFMAs).
     const int wq = w & 3;
     const int voff_a4 = (int)((wq * 8 + ld_lrow) * p.lda) + ld_kchunk * 16;
     const int voff_b4 = (int)((wq * 8 + ld_lrow) * p.ldb) + ld_kchunk * 16;

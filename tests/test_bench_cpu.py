@@ -50,3 +50,12 @@ def test_counter_traffic_without_a_summary_is_none():
     assert bench.counter_traffic("linear_fwd_256x512x256", "gemm_fwd") is None
     assert bench.counter_traffic("dense_8192x4096x4096", "no_such_kernel") is None
     assert bench.kernel_source_hash("no_such_kernel<0>") is None
+
+
+def test_source_hash_ignores_comments_but_not_code():
+    code = 'int a = 1; // note\n/* block\n  note */ const char* s = "x // kept"; char q = \'"\'; a /= 2;\n'
+    assert bench._code_only(code) == 'int a = 1; const char* s = "x // kept"; char q = \'"\'; a /= 2;'
+    # a comment edit and a whitespace change leave the code unchanged; a code edit does not
+    assert bench._code_only(code.replace("note", "other words")) == bench._code_only(code)
+    assert bench._code_only(code.replace("a = 1;", "a  =\n 1;")) == bench._code_only(code)
+    assert bench._code_only(code.replace("a /= 2", "a /= 3")) != bench._code_only(code)
