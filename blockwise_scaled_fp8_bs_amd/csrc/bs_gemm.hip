@@ -676,10 +676,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
     // wave while the CU's address unit works through them (about 1 KiB per
     // 16 cycles); with one group issuing per K block, the other group's
     // waves go straight to their MFMAs and keep the matrix pipes busy.  The
-    // 1x128 x 1x128 and MX kernels issue this way, at the start of each
-    // block: every wave issuing its share there was 1.5-3 % slower, and so
-    // was splitting the wgrad's copies (A by the group at the block start,
-    // B by every wave after one of its first MFMAs).
+    // MX kernel issues this way at the start of each block, the 1x128 x
+    // 1x128 kernel after its first two MFMAs (kLateIssue): every wave
+    // issuing its share at the block start was 1.5-3 % slower, and so was
+    // splitting the wgrad's copies (A by the group at the block start, B by
+    // every wave after one of its first MFMAs).
     const int wq = w & 3;
     const int voff_a4 = (int)((wq * 8 + ld_lrow) * p.lda) + ld_kchunk * 16;
     const int voff_b4 = (int)((wq * 8 + ld_lrow) * p.ldb) + ld_kchunk * 16;
@@ -706,6 +707,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
     // no registers: spreading its copies spills, and measured no gain); so
     // does the MX kernel (shared spread issue 4 % slower).
     constexpr bool kSpread = !MX && !B1X128 && KIND != kGroupK;
+    // The 1x128 x 1x128 kernel's issuing group takes its copies after its
+    // first two MFMAs (and the first fold) instead of before them, so the
+    // matrix pipes start on both waves' work at the block start: about 1 %
+    // faster on the MoE and FFN wgrads (after the first MFMA: 0.8 % slower,
+    // after the fifth: 4 % slower).
+    constexpr bool kLateIssue = !kSpread && !MX;
     // An MFMA operand fragment: logical chunks 2 lg and 2 lg + 1 of the row
     // (for MX, K chunks lg and lg + 4: see the copies above).
     auto frag = [&](const uint8_t* base, int row) -> v8i {
@@ -761,7 +768,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
         for (int32_t it = 0; it < nkb; ++it) {
             const bool spread = kSpread && it + 1 < nkb;
             if (it + 1 < nkb) {
-                if (!kSpread) issue_loads_group(ops, cur.kb0 + it + 1, s ^ 1, it & 1);
+                if (!kSpread && !kLateIssue) issue_loads_group(ops, cur.kb0 + it + 1, s ^ 1, it & 1);
             } else if (has_next) {
                 load_next(s ^ 1);
             }
@@ -836,6 +843,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
                             issue_copy(ops, cur.kb0 + it + 1, s ^ 1, q);
                         }
                         if (q > 0) fold(pbuf[(q - 1) & 1], pi, pj);
+                        if (kLateIssue && q == 1 && it + 1 < nkb)
+                            issue_loads_group(ops, cur.kb0 + it + 1, s ^ 1, it & 1);
                         pi = i;
                         pj = j;
                     }
