@@ -696,9 +696,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
     };
     // With 128x128 B scales (forward and dgrad) all eight waves share the
     // next K block's copies instead: wave w issues its issue_copy pieces, one
-    // after each of its first 8 MFMAs (waves 0 and 1 the scales with the
-    // first), so every copy is still issued in the first quarter of the
-    // block.  Both waves of a SIMD then carry the same load and reach the
+    // after each of 8 consecutive MFMAs from its first (GROUP_M: its third;
+    // waves 0 and 1 the scales with the first piece), so every copy is still
+    // issued in the first third of the block.  Both waves of a SIMD then carry the same load and reach the
     // block-end barrier together: with one group issuing, the other group
     // spent 16-24 % of its time waiting there, and the shared issue is 3-5 %
     // faster on the forward (the one-group spread was itself 3-4 % faster
@@ -707,6 +707,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
     // no registers: spreading its copies spills, and measured no gain); so
     // does the MX kernel (shared spread issue 4 % slower).
     constexpr bool kSpread = !MX && !B1X128 && KIND != kGroupK;
+    // GROUP_M starts its share after its third MFMA rather than its first
+    // (MoE forward and dgrad 1 % faster over five alternating runs; the
+    // dense GEMMs were not faster so).
+    constexpr int kSpreadAt = KIND == kGroupM ? 2 : 0;
     // The 1x128 x 1x128 kernel's issuing group takes its copies after its
     // first two MFMAs (and the first fold) instead of before them, so the
     // matrix pipes start on both waves' work at the block start: about 1 %
@@ -838,9 +842,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
                         const int q = i * TN + j;
                         pbuf[q & 1] =
                             __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, zero, 0, 0, 0, 0, 0, 0);
-                        if (kSpread && q < 8 && spread) {
-                            if (q == 0) issue_scales(ops, cur.kb0 + it + 1, s ^ 1, 0);
-                            issue_copy(ops, cur.kb0 + it + 1, s ^ 1, q);
+                        if (kSpread && q >= kSpreadAt && q < kSpreadAt + 8 && spread) {
+                            if (q == kSpreadAt) issue_scales(ops, cur.kb0 + it + 1, s ^ 1, 0);
+                            issue_copy(ops, cur.kb0 + it + 1, s ^ 1, q - kSpreadAt);
                         }
                         if (q > 0) fold(pbuf[(q - 1) & 1], pi, pj);
                         if (kLateIssue && q == 1 && it + 1 < nkb)
