@@ -23,8 +23,10 @@ between kernels cost GPU time of their own).  The CPU oracle is timed on a
 bounded sample of the same workload on the host (rank 0, N = 1).
 
 The line also carries: the SHA-256 of the bf16 inputs (the bytes both the
-GPU and the oracle consume), the shader and memory clocks sampled while the
-timed steps ran, a short record of each dense workload (forward, dgrad
+GPU and the oracle consume), the shader and memory clocks read while the
+timed steps ran (the driver updates them about once a second; where fewer
+than two updates fall in the timed steps, the same steps keep running
+untimed until two have come), a short record of each dense workload (forward, dgrad
 and wgrad of one linear layer) timed the same way, and the smallest layer's
 forward (256x512x256, launch-bound) as eager calls and as one HIP graph.
 """
@@ -510,6 +512,7 @@ class ClockSampler:
         self.samples = []
         self.error = None
         self.handle = None
+        self.extra_steps = 0
         self._stop = threading.Event()
         self._thread = None
         try:
@@ -532,11 +535,18 @@ class ClockSampler:
             self.error = f"{type(e).__name__}: {e}"
 
     def _read(self):
+        """(table timestamp, mean GFX clock over the XCDs, UCLK).  The
+        driver refreshes its metrics table about once a second, so reads in
+        between repeat the last update; the timestamp tells updates apart."""
         m = self.smi.amdsmi_get_gpu_metrics_info(self.handle)
+        ts = m.get("firmware_timestamp")
+        if not isinstance(ts, int):
+            ts = m.get("system_clock_counter")
         xcd = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
         g = sum(xcd) / len(xcd) if xcd else m.get("current_gfxclk")
         u = m.get("current_uclk")
-        return (float(g) if isinstance(g, (int, float)) else None,
+        return (ts if isinstance(ts, int) else None,
+                float(g) if isinstance(g, (int, float)) else None,
                 float(u) if isinstance(u, (int, float)) else None)
 
     def _run(self):
@@ -552,9 +562,26 @@ class ClockSampler:
         import threading
         if self.handle is None:
             return
+        try:
+            self.ts0 = self._read()[0]  # the update current before the work starts
+        except Exception as e:
+            self.error = f"{type(e).__name__}: {e}"
+            return
         self._stop.clear()
         self._thread = threading.Thread(target=self._run, daemon=True)
         self._thread.start()
+
+    def fresh(self):
+        """Samples of metric-table updates made after start(), one per update
+        (every sample when the driver gives no timestamp)."""
+        out, seen = [], {getattr(self, "ts0", None)}
+        for ts, g, u in self.samples:
+            if ts is None:
+                out.append((g, u))
+            elif ts not in seen:
+                seen.add(ts)
+                out.append((g, u))
+        return out
 
     def stop(self):
         if self._thread is not None:
@@ -562,17 +589,20 @@ class ClockSampler:
             self._thread.join()
             self._thread = None
 
-    def summary(self):
+    def summary(self, extra_steps=0):
         import statistics
-        g = [s[0] for s in self.samples if s[0]]
-        u = [s[1] for s in self.samples if s[1]]
+        fresh = self.fresh()
+        g = [x[0] for x in fresh if x[0]]
+        u = [x[1] for x in fresh if x[1]]
+        where = "the timed steps" + (f" and {extra_steps} further untimed steps" if extra_steps else "")
+        src = ("amdsmi gpu metrics (current_gfxclks averaged over XCDs, current_uclk), one sample per update of "
+               "the driver's metrics table (about once a second) during " + where)
         if not g:
-            return {"sclk_mhz": None, "mclk_mhz": None, "samples": 0, "error": self.error,
-                    "source": "amdsmi gpu metrics (current_gfxclks averaged over XCDs, current_uclk)"}
+            return {"sclk_mhz": None, "mclk_mhz": None, "samples": 0,
+                    "error": self.error or "the metrics table was not updated while the work ran", "source": src}
         return {"sclk_mhz": round(statistics.median(g)), "sclk_min_mhz": round(min(g)),
                 "sclk_max_mhz": round(max(g)), "mclk_mhz": round(statistics.median(u)) if u else None,
-                "samples": len(g), "source": "amdsmi gpu metrics (current_gfxclks averaged over XCDs, "
-                                             "current_uclk), sampled every 5 ms during the timed steps"}
+                "samples": len(g), "source": src}
 
 
 def time_step(step, steps, warmup, stream, clocks=None):
@@ -620,6 +650,14 @@ def time_step(step, steps, warmup, stream, clocks=None):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     if clocks is not None:
+        # the driver updates its clock readings about once a second: when the
+        # timed steps were shorter than two updates, the same steps keep
+        # running (untimed) until two more have come or 3 s have passed
+        t_end = time.perf_counter() + 3.0
+        while clocks.handle is not None and len(clocks.fresh()) < 2 and time.perf_counter() < t_end:
+            run_step()
+            torch.cuda.synchronize()
+            clocks.extra_steps += 1
         clocks.stop()
     ms_per_step = (t1 - t0) * 1e3 / steps
     dom_ms = sum(e[0][0].elapsed_time(e[0][1]) for e in ev_dom) / steps
@@ -973,7 +1011,7 @@ def main():
         "gemm_frac_of_peak": round(summ["gemm_tflops"] / FP8_PEAK_TFLOPS, 4),
         "quant_gbs": round(summ["quant_gbs"], 1),
         "quant_frac_of_hbm": round(summ["quant_gbs"] / HBM_PEAK_GBS, 4),
-        "clocks": clocks.summary(),
+        "clocks": clocks.summary(clocks.extra_steps),
         "inputs_sha256": digest,
         "hbm_copy_gbs": None if copy_gbs is None else round(copy_gbs, 1),
         "quant_frac_of_copy": None if copy_gbs is None else round(summ["quant_gbs"] / copy_gbs, 4),

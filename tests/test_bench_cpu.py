@@ -59,3 +59,19 @@ def test_source_hash_ignores_comments_but_not_code():
     assert bench._code_only(code.replace("note", "other words")) == bench._code_only(code)
     assert bench._code_only(code.replace("a = 1;", "a  =\n 1;")) == bench._code_only(code)
     assert bench._code_only(code.replace("a /= 2", "a /= 3")) != bench._code_only(code)
+
+
+def test_clock_samples_count_each_table_update_once():
+    # the driver's metrics table changes about once a second; repeated reads of
+    # one update, and the update current before the work started, are not samples
+    c = bench.ClockSampler.__new__(bench.ClockSampler)
+    c.ts0, c.error, c.extra_steps = 100, None, 0
+    c.samples = [(100, 250.0, 1900.0), (100, 250.0, 1900.0), (200, 2000.0, 2000.0), (200, 2000.0, 2000.0),
+                 (300, 1900.0, 2000.0)]
+    assert c.fresh() == [(2000.0, 2000.0), (1900.0, 2000.0)]
+    summ = c.summary(extra_steps=3)
+    assert summ["samples"] == 2 and summ["sclk_mhz"] == 1950 and summ["sclk_min_mhz"] == 1900
+    assert "3 further untimed steps" in summ["source"]
+    c.samples = [(100, 250.0, 1900.0)]
+    summ = c.summary()
+    assert summ["sclk_mhz"] is None and summ["samples"] == 0 and "not updated" in summ["error"]
