@@ -151,8 +151,20 @@ def test_b_kinds_agree_on_expanded_scales():
 
 @pytest.mark.parametrize("sizes", [(128, 0, 256), (256, 384, 128, 0), (0, 0, 512), (200, 56, 300)])
 def test_group_m(sizes):
+    _group_m_case(sizes, 640)
+
+
+# one and three K blocks: the next block's copies are shared out over MFMAs
+# that a one-block tile never reaches, and a three-block tile only in its
+# first two blocks
+@pytest.mark.parametrize("K", [128, 384])
+def test_group_m_short_k(K):
+    _group_m_case((256, 128, 384), K)
+
+
+def _group_m_case(sizes, K):
     need_gpu()
-    G, N, K = len(sizes), 384, 640
+    G, N = len(sizes), 384
     ends = np.cumsum(sizes).astype(np.int32)
     M = int(ends[-1])
     qa, sa = operand_1x128(M, K, 1.0, seed=M + G)
@@ -163,7 +175,7 @@ def test_group_m(sizes):
     sb_view = torch.as_strided(sw_gpu, (G, K // 128, N // 128), (N // 128, sw_gpu.stride(0), 1))
     qb = torch.from_numpy(qw).cuda().view(G, N, K)
     full, out = guarded(M, N, torch.bfloat16)
-    print(f"group_m sizes={sizes}", flush=True)
+    print(f"group_m sizes={sizes} K={K}", flush=True)
     bs.bs_grouped_scaled_mm(bs.BS_GROUP_M, torch.from_numpy(ends).cuda(), torch.from_numpy(qa).cuda(),
                             to_gpu_scales(sa), qb, sb_view, bs.BS_SCALE_128X128, out=out)
     torch.cuda.synchronize()
