@@ -677,7 +677,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
     // 16 cycles); with one group issuing per K block, the other group's
     // waves go straight to their MFMAs and keep the matrix pipes busy.  The
     // MX kernel issues this way at the start of each block, the 1x128 x
-    // 1x128 kernel after its first two MFMAs (kLateIssue): every wave
+    // 1x128 kernel in two halves after its first MFMAs (kLateIssue): every wave
     // issuing its share at the block start was 1.5-3 % slower, and so was
     // splitting the wgrad's copies (A by the group at the block start, B by
     // every wave after one of its first MFMAs).
@@ -693,6 +693,18 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
             dma16(o.b, lds_addr(&sm.b[s][(4 * i + wq) * 1024]), voff_b4, k_off + (int)(32 * i * p.ldb));
         }
         issue_scales(o, kb, s, 4 * g);
+    };
+    // Half h of issue_loads_group's copies (rounds 4h .. 4h + 3; the scales
+    // with the first half).
+    auto issue_loads_group_half = [&](const Operands& o, int32_t kb, int s, int g, int h) {
+        if ((w >> 2) != g) return;
+        const int k_off = kb * BK;
+#pragma unroll
+        for (int i = 4 * h; i < 4 * h + 4; ++i) {
+            dma16(o.a, lds_addr(&sm.a[s][(4 * i + wq) * 1024]), voff_a4, k_off + (int)(32 * i * p.lda));
+            dma16(o.b, lds_addr(&sm.b[s][(4 * i + wq) * 1024]), voff_b4, k_off + (int)(32 * i * p.ldb));
+        }
+        if (h == 0) issue_scales(o, kb, s, 4 * g);
     };
     // With 128x128 B scales (forward and dgrad) all eight waves share the
     // next K block's copies instead: wave w issues its issue_copy pieces, one
@@ -712,10 +724,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
     // dense GEMMs were not faster so).
     constexpr int kSpreadAt = KIND == kGroupM ? 2 : 0;
     // The 1x128 x 1x128 kernel's issuing group takes its copies after its
-    // first two MFMAs (and the first fold) instead of before them, so the
-    // matrix pipes start on both waves' work at the block start: about 1 %
-    // faster on the MoE and FFN wgrads (after the first MFMA: 0.8 % slower,
-    // after the fifth: 4 % slower).
+    // first MFMAs instead of before them, so the matrix pipes start on both
+    // waves' work at the block start: half after its second MFMA (and the
+    // first fold), half after its fourth.  Against all of them before the
+    // first MFMA: MoE and FFN wgrads about 2 % faster (all after the second
+    // MFMA: 1 %; after the first: 0.8 % slower; after the fifth: 4 % slower).
     constexpr bool kLateIssue = !kSpread && !MX;
     // An MFMA operand fragment: logical chunks 2 lg and 2 lg + 1 of the row
     // (for MX, K chunks lg and lg + 4: see the copies above).
@@ -847,8 +860,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
                             issue_copy(ops, cur.kb0 + it + 1, s ^ 1, q - kSpreadAt);
                         }
                         if (q > 0) fold(pbuf[(q - 1) & 1], pi, pj);
-                        if (kLateIssue && q == 1 && it + 1 < nkb)
-                            issue_loads_group(ops, cur.kb0 + it + 1, s ^ 1, it & 1);
+                        if (kLateIssue && (q == 1 || q == 3) && it + 1 < nkb)
+                            issue_loads_group_half(ops, cur.kb0 + it + 1, s ^ 1, it & 1, q == 1 ? 0 : 1);
                         pi = i;
                         pj = j;
                     }
