@@ -725,10 +725,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
     constexpr int kSpreadAt = KIND == kGroupM ? 2 : 0;
     // The 1x128 x 1x128 kernel's issuing group takes its copies after its
     // first MFMAs instead of before them, so the matrix pipes start on both
-    // waves' work at the block start: half after its second MFMA (and the
-    // first fold), half after its fourth.  Against all of them before the
-    // first MFMA: MoE and FFN wgrads about 2 % faster (all after the second
-    // MFMA: 1 %; after the first: 0.8 % slower; after the fifth: 4 % slower).
+    // waves' work at the block start: half after its third MFMA, half after
+    // its fifth.  Against all of them before the first MFMA: MoE wgrad about
+    // 3 %, FFN-up wgrad 2 % faster.  Measured alternatives, all slower: all
+    // copies after the first, second or fifth MFMA; halves after the second
+    // and third, second and fourth, third and fourth, or second and fifth
+    // MFMAs; quarters after the second to fifth; a half after the sixth
+    // MFMA made the compiler spill.
     constexpr bool kLateIssue = !kSpread && !MX;
     // An MFMA operand fragment: logical chunks 2 lg and 2 lg + 1 of the row
     // (for MX, K chunks lg and lg + 4: see the copies above).
@@ -860,8 +863,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
                             issue_copy(ops, cur.kb0 + it + 1, s ^ 1, q - kSpreadAt);
                         }
                         if (q > 0) fold(pbuf[(q - 1) & 1], pi, pj);
-                        if (kLateIssue && (q == 1 || q == 3) && it + 1 < nkb)
-                            issue_loads_group_half(ops, cur.kb0 + it + 1, s ^ 1, it & 1, q == 1 ? 0 : 1);
+                        if (kLateIssue && (q == 2 || q == 4) && it + 1 < nkb)
+                            issue_loads_group_half(ops, cur.kb0 + it + 1, s ^ 1, it & 1, q == 2 ? 0 : 1);
                         pi = i;
                         pj = j;
                     }
