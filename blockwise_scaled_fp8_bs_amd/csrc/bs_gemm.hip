@@ -710,14 +710,16 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
     // next K block's copies instead: wave w issues its issue_copy pieces, one
     // after each of 8 consecutive MFMAs from its first (GROUP_M: its third;
     // waves 0 and 1 the scales with the first piece), so every copy is still
-    // issued in the first third of the block.  Both waves of a SIMD then carry the same load and reach the
-    // block-end barrier together: with one group issuing, the other group
-    // spent 16-24 % of its time waiting there, and the shared issue is 3-5 %
-    // faster on the forward (the one-group spread was itself 3-4 % faster
-    // than issuing every copy before the first MFMA).  The 1x128 x 1x128
-    // kernel keeps the block issue by one group (its per-element fold leaves
-    // no registers: spreading its copies spills, and measured no gain); so
-    // does the MX kernel (shared spread issue 4 % slower).
+    // issued in the first third of the block.  Both waves of a SIMD then
+    // carry the same load and reach the block-end barrier together: with one
+    // group issuing, the other group spent 16-24 % of its time waiting
+    // there, and the shared issue is 3-5 % faster on the forward (the
+    // one-group spread was itself 3-4 % faster than issuing every copy
+    // before the first MFMA).  The 1x128 x 1x128 kernel keeps the issue by
+    // one group (its per-element fold leaves no registers: spreading its
+    // copies one per MFMA spills, and the shared spread measured no gain),
+    // in two bursts after its first MFMAs (kLateIssue); the MX kernel keeps
+    // it at the block start (its shared spread was 4 % slower).
     constexpr bool kSpread = !MX && !B1X128 && KIND != kGroupK;
     // GROUP_M starts its share after its third MFMA rather than its first
     // (MoE forward and dgrad 1 % faster over five alternating runs; the
@@ -728,10 +730,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
     // waves' work at the block start: half after its third MFMA, half after
     // its fifth.  Against all of them before the first MFMA: MoE wgrad about
     // 3 %, FFN-up wgrad 2 % faster.  Measured alternatives, all slower: all
-    // copies after the first, second or fifth MFMA; halves after the second
-    // and third, second and fourth, third and fourth, or second and fifth
-    // MFMAs; quarters after the second to fifth; a half after the sixth
-    // MFMA made the compiler spill.
+    // copies after the first, second, third or fifth MFMA; halves after the
+    // second and fourth, third and fourth, fourth and fifth, or second and
+    // fifth MFMAs; quarters after the second to fifth; a half after the
+    // sixth MFMA made the compiler spill.
     constexpr bool kLateIssue = !kSpread && !MX;
     // An MFMA operand fragment: logical chunks 2 lg and 2 lg + 1 of the row
     // (for MX, K chunks lg and lg + 4: see the copies above).
