@@ -367,6 +367,44 @@ def test_persistent_group_k_many_tiles():
     assert torch.all(out_full[G] == 5.0)
 
 
+def test_persistent_group_k_exact_many_k_blocks():
+    """GROUP_K with an empty group, more tiles than workgroups and 5 to 15 K
+    blocks per group, on exact small-integer arithmetic (codes |v| <= 3,
+    scales 2^[-2, 2]: every partial sum, at most 2^19, is exact in fp32):
+    the wgrad's copies, issued in two halves after the issuing group's first
+    MFMAs, must put every K block of every group in the right stage; each
+    group's output equals the float64 oracle bit for bit."""
+    need_gpu()
+    rng = np.random.default_rng(8)
+    sizes = (1024, 0, 1920, 640, 1408)
+    G, M, N = len(sizes), 2304, 2048                   # 9 x 8 tiles per group, 288 in all
+    ends = np.cumsum(sizes).astype(np.int32)
+    T = int(ends[-1])
+    qa = rng.choice(SMALL_INT_CODES, size=(M, T))
+    qb = rng.choice(SMALL_INT_CODES, size=(N, T))
+    sa = np.exp2(rng.integers(-2, 3, size=(M, T // 128))).astype(np.float32)
+    sb = np.exp2(rng.integers(-2, 3, size=(N, T // 128))).astype(np.float32)
+    out_full = torch.full((G + 1, M, N), 5.0, dtype=torch.float32, device="cuda")
+    out = out_full[:G]
+    print(f"persistent exact group_k sizes={sizes} M={M} N={N}", flush=True)
+    bs.bs_grouped_scaled_mm(bs.BS_GROUP_K, torch.from_numpy(ends).cuda(), torch.from_numpy(qa).cuda(),
+                            to_gpu_scales(sa), torch.from_numpy(qb).cuda(), to_gpu_scales(sb),
+                            bs.BS_SCALE_1X128, out=out)
+    torch.cuda.synchronize()
+    d = out.cpu().numpy().astype(np.float64)
+    start = 0
+    for g, e in enumerate(ends):
+        if e == start:
+            assert np.all(d[g] == 0), f"empty group {g} must be zeros"
+        else:
+            a = gemm.dequant(qa[:, start:e], sa[:, start // 128:e // 128], 1)
+            b = gemm.dequant(qb[:, start:e], sb[:, start // 128:e // 128], 1)
+            bad = np.argwhere(d[g] != a @ b.T)
+            assert bad.size == 0, f"group {g}: {len(bad)} inexact elements, first {bad[0]}"
+        start = e
+    assert torch.all(out_full[G] == 5.0)
+
+
 def test_group_k_more_groups_than_ranked():
     """GROUP_K with more groups than the kernel ranks by size (256): the
     tiles then follow the natural group order."""
