@@ -676,8 +676,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
     // wave while the CU's address unit works through them (about 1 KiB per
     // 16 cycles); with one group issuing per K block, the other group's
     // waves go straight to their MFMAs and keep the matrix pipes busy.  The
-    // MX kernel issues this way at the start of each block, the 1x128 x
-    // 1x128 kernel in two halves after its first MFMAs (kLateIssue): every wave
+    // MX kernel issues this way at the start of each block, the others but
+    // GROUP_M in two halves after the first MFMAs (kLateIssue): every wave
     // issuing its share at the block start was 1.5-3 % slower, and so was
     // splitting the wgrad's copies (A by the group at the block start, B by
     // every wave after one of its first MFMAs).
@@ -706,34 +706,36 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
         }
         if (h == 0) issue_scales(o, kb, s, 4 * g);
     };
-    // With 128x128 B scales (forward and dgrad) all eight waves share the
-    // next K block's copies instead: wave w issues its issue_copy pieces, one
-    // after each of 8 consecutive MFMAs from its first (GROUP_M: its third;
-    // waves 0 and 1 the scales with the first piece), so every copy is still
-    // issued in the first third of the block.  Both waves of a SIMD then
-    // carry the same load and reach the block-end barrier together: with one
-    // group issuing, the other group spent 16-24 % of its time waiting
-    // there, and the shared issue is 3-5 % faster on the forward (the
-    // one-group spread was itself 3-4 % faster than issuing every copy
-    // before the first MFMA).  The 1x128 x 1x128 kernel keeps the issue by
-    // one group (its per-element fold leaves no registers: spreading its
-    // copies one per MFMA spills, and the shared spread measured no gain),
-    // in two bursts after its first MFMAs (kLateIssue); the MX kernel keeps
-    // it at the block start (its shared spread was 4 % slower).
-    constexpr bool kSpread = !MX && !B1X128 && KIND != kGroupK;
-    // GROUP_M starts its share after its third MFMA rather than its first
-    // (MoE forward and dgrad 1 % faster over five alternating runs; the
-    // dense GEMMs were not faster so).
-    constexpr int kSpreadAt = KIND == kGroupM ? 2 : 0;
-    // The 1x128 x 1x128 kernel's issuing group takes its copies after its
-    // first MFMAs instead of before them, so the matrix pipes start on both
-    // waves' work at the block start: half after its third MFMA, half after
-    // its fifth.  Against all of them before the first MFMA: MoE wgrad about
-    // 3 %, FFN-up wgrad 2 % faster.  Measured alternatives, all slower: all
-    // copies after the first, second, third or fifth MFMA; halves after the
-    // second and fourth, third and fourth, fourth and fifth, or second and
-    // fifth MFMAs; quarters after the second to fifth; a half after the
-    // sixth MFMA made the compiler spill.
+    // GROUP_M (MoE forward and dgrad, 128x128 B scales) has all eight waves
+    // share the next K block's copies instead: wave w issues its issue_copy
+    // pieces, one after each of its third to tenth MFMAs (waves 0 and 1 the
+    // scales with the first piece), so every copy is still issued in the
+    // first third of the block.  Both waves of a SIMD then carry the same
+    // load and reach the block-end barrier together: with one group issuing,
+    // the other group spent 16-24 % of its time waiting there.  The shared
+    // spread is 3-5 % faster than one group spreading its copies over its
+    // first MFMAs (itself 3-4 % faster than issuing every copy before the
+    // first MFMA) and 1.2 % faster on the MoE forward than one group's
+    // copies in two bursts (kLateIssue); starting it after the first MFMA
+    // was 1 % slower, after the fourth or fifth 1-2 % slower.  The MX kernel
+    // keeps the one-group issue at the block start (its shared spread was
+    // 4 % slower).
+    constexpr bool kSpread = !MX && !B1X128 && KIND == kGroupM;
+    constexpr int kSpreadAt = 2;
+    // The other kernels' issuing group takes its copies after its first
+    // MFMAs instead of before them, so the matrix pipes start on both waves'
+    // work at the block start: half after its third MFMA, half after its
+    // fifth.  For the 1x128 x 1x128 wgrad (whose per-element fold leaves no
+    // registers for a spread: one copy per MFMA spills), against all copies
+    // before the first MFMA: MoE wgrad about 3 %, FFN-up wgrad 2 % faster;
+    // measured alternatives, all slower: all copies after the first, second,
+    // third or fifth MFMA; halves after the second and fourth, third and
+    // fourth, fourth and fifth, or second and fifth MFMAs; quarters after
+    // the second to fifth; a half after the sixth MFMA made the compiler
+    // spill.  For the dense forward and dgrad (128x128 B scales), against
+    // the shared spread from the first MFMA: 8192x4096x4096 and
+    // 16384x5120x8192 forward 3.3-3.6 % faster, dgrads and the
+    // 16384x7168x2048 GEMMs within 0.7 %.
     constexpr bool kLateIssue = !kSpread && !MX;
     // An MFMA operand fragment: logical chunks 2 lg and 2 lg + 1 of the row
     // (for MX, K chunks lg and lg + 4: see the copies above).
